@@ -1,0 +1,236 @@
+// C ABI of the library (declared in include/mcs.h): argument validation on
+// the host before anything is enqueued, workspace sizing, kernel dispatch.
+// Stateless: every buffer is the caller's, nothing is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <initializer_list>
+#include <string>
+
+#include "mcs.h"
+#include "mcs_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mcs_status fail(mcs_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mcs_status ok() {
+  g_last_error.clear();
+  return MCS_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Checked {
+  mcs::Shape s;
+  bool bf16;
+  bool empty;
+};
+
+// Pure host checks of the problem description.
+mcs_status check_problem(const mcs_problem* p, Checked& out) {
+  if (!p) return fail(MCS_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B < 0 || p->H < 0) return fail(MCS_ERR_INVALID_ARG, "B=%d H=%d must be >= 0", p->B, p->H);
+  if ((long long)p->B * p->H > 65535)
+    return fail(MCS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)p->B * p->H);
+  if (p->Nq < 0 || p->Nq > (1 << 24)) return fail(MCS_ERR_INVALID_ARG, "Nq=%d outside [0, 2^24]", p->Nq);
+  if (p->Nkv < 1 || p->Nkv > (1 << 24)) return fail(MCS_ERR_INVALID_ARG, "Nkv=%d outside [1, 2^24]", p->Nkv);
+  if (p->d != 64 && p->d != 128) return fail(MCS_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", p->d);
+  if (p->group_size != 64 && p->group_size != 128)
+    return fail(MCS_ERR_UNSUPPORTED, "group_size=%d (supported: 64, 128)", p->group_size);
+  if (p->k < 1 || p->k > p->Nkv) return fail(MCS_ERR_INVALID_ARG, "k=%d outside [1, Nkv=%d]", p->k, p->Nkv);
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f))
+    return fail(MCS_ERR_INVALID_ARG, "scale=%g must be finite and > 0", (double)p->scale);
+  if (p->causal_block < 0) return fail(MCS_ERR_INVALID_ARG, "causal_block=%d < 0", p->causal_block);
+  if (p->q_offset < 0 || p->q_offset > (1 << 30))
+    return fail(MCS_ERR_INVALID_ARG, "q_offset=%d outside [0, 2^30]", p->q_offset);
+  if (p->pddp_iters < 0 || p->pddp_iters > 1024)
+    return fail(MCS_ERR_INVALID_ARG, "pddp_iters=%d outside [0, 1024]", p->pddp_iters);
+  if (p->dtype != MCS_F32 && p->dtype != MCS_BF16) return fail(MCS_ERR_UNSUPPORTED, "dtype=%d", p->dtype);
+  const long long bh = (long long)p->B * p->H;
+  const long long nmax = p->Nq > p->Nkv ? p->Nq : p->Nkv;
+  if (bh * nmax * p->d >= (1LL << 40)) return fail(MCS_ERR_UNSUPPORTED, "tensor sizes exceed 2^40 elements");
+  const int c = (p->Nq + p->group_size - 1) / p->group_size;
+  out.s = mcs::Shape{(int)bh,  p->Nq, p->Nkv, p->d, p->group_size, p->k, c, p->scale, p->causal_block,
+                     p->q_offset, p->pddp_iters};
+  out.bf16 = p->dtype == MCS_BF16;
+  out.empty = bh == 0 || p->Nq == 0;
+  return MCS_OK;
+}
+
+mcs_status check_host_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(MCS_ERR_INVALID_ARG, "%s is NULL", name);
+  if ((uintptr_t)ptr % 16) return fail(MCS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MCS_OK;
+}
+
+// Device-residency check (a HIP runtime query, no GPU work).
+mcs_status check_dev_ptr(const void* ptr, const char* name) {
+  hipPointerAttribute_t a;
+  const hipError_t e = hipPointerGetAttributes(&a, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MCS_ERR_INVALID_ARG, "%s is not device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+    return fail(MCS_ERR_INVALID_ARG, "%s is not device memory", name);
+  return MCS_OK;
+}
+
+struct Ptr {
+  const void* p;
+  const char* name;
+  bool optional;
+};
+
+mcs_status check_ptrs(std::initializer_list<Ptr> ptrs) {
+  for (const Ptr& x : ptrs) {
+    if (x.optional && !x.p) continue;
+    if (mcs_status s = check_host_ptr(x.p, x.name)) return s;
+  }
+  for (const Ptr& x : ptrs) {
+    if (x.optional && !x.p) continue;
+    if (mcs_status s = check_dev_ptr(x.p, x.name)) return s;
+  }
+  return MCS_OK;
+}
+
+size_t anchor_lse_bytes(const mcs::Shape& s) { return round_up((size_t)s.BH * s.Nq * 4); }
+size_t anchor_mass_bytes_per_head(const mcs::Shape& s) { return round_up((size_t)s.c * s.Nkv * 4); }
+
+mcs_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MCS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mcs_status_string(mcs_status s) {
+  switch (s) {
+    case MCS_OK: return "MCS_OK";
+    case MCS_ERR_INVALID_ARG: return "MCS_ERR_INVALID_ARG";
+    case MCS_ERR_UNSUPPORTED: return "MCS_ERR_UNSUPPORTED";
+    case MCS_ERR_WORKSPACE: return "MCS_ERR_WORKSPACE";
+    case MCS_ERR_HIP: return "MCS_ERR_HIP";
+  }
+  return "MCS_ERR_UNKNOWN";
+}
+
+const char* mcs_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mcs_version(void) { return 100; }
+
+mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes, size_t* min_bytes) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (!bytes) return fail(MCS_ERR_INVALID_ARG, "bytes is NULL");
+  size_t need = 0, need_min = 0;
+  if (kind == MCS_WS_GROUP) {
+    need = need_min = c.empty ? 0 : mcs::pddp_workspace_bytes(c.s);
+  } else if (kind == MCS_WS_ANCHOR) {
+    if (!c.empty) {
+      need = anchor_lse_bytes(c.s) + (size_t)c.s.BH * anchor_mass_bytes_per_head(c.s);
+      need_min = anchor_lse_bytes(c.s) + anchor_mass_bytes_per_head(c.s);
+    }
+  } else {
+    return fail(MCS_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
+  }
+  *bytes = need;
+  if (min_bytes) *min_bytes = need_min;
+  return ok();
+}
+
+mcs_status mcs_group(const mcs_problem* p, const void* Q, int32_t* perm, void* ws, size_t ws_bytes,
+                     void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (c.empty) return ok();
+  const size_t need = mcs::pddp_workspace_bytes(c.s);
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {perm, "perm", false}, {ws, "ws", false}})) return s;
+  if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "group workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(mcs::launch_pddp(c.s, c.bf16, Q, perm, ws, (hipStream_t)stream), "mcs_group");
+}
+
+mcs_status mcs_dense_attn(const mcs_problem* p, const void* Q, const void* K, const void* V, void* O,
+                          float* lse, void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (c.empty) return ok();
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {O, "O", false},
+                                 {lse, "lse", true}}))
+    return s;
+  if (O == Q || O == K || O == V) return fail(MCS_ERR_INVALID_ARG, "O aliases an input");
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = c.bf16 ? mcs::launch_dense_bf16(c.s, Q, K, V, O, lse, nullptr, st)
+                              : mcs::launch_dense_f32(c.s, Q, K, V, O, lse, nullptr, st);
+  return hip_status(e, "mcs_dense_attn");
+}
+
+mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const void* V,
+                      const int32_t* perm, void* O, int32_t* idx, float* R, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (c.empty) return ok();
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {perm, "perm", false},
+                                 {O, "O", false}, {idx, "idx", false}, {R, "R", false}, {ws, "ws", false}}))
+    return s;
+  if (O == Q || O == K || O == V || (void*)R == O || (void*)R == Q || (void*)R == K || (void*)R == V)
+    return fail(MCS_ERR_INVALID_ARG, "an output aliases another argument");
+  const size_t lse_b = anchor_lse_bytes(c.s), head_b = anchor_mass_bytes_per_head(c.s);
+  if (ws_bytes < lse_b + head_b)
+    return fail(MCS_ERR_WORKSPACE, "anchor workspace %zu < minimum %zu bytes", ws_bytes, lse_b + head_b);
+  const size_t fit = (ws_bytes - lse_b) / head_b;
+  const int chunk = fit >= (size_t)c.s.BH ? c.s.BH : (int)fit;
+  float* lse = (float*)ws;
+  float* mass = (float*)((char*)ws + lse_b);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = c.bf16 ? mcs::launch_dense_bf16(c.s, Q, K, V, O, lse, R, st)
+                        : mcs::launch_dense_f32(c.s, Q, K, V, O, lse, R, st);
+  if (e != hipSuccess) return hip_status(e, "mcs_anchor (dense)");
+  for (int bh0 = 0; bh0 < c.s.BH; bh0 += chunk) {
+    const int nbh = c.s.BH - bh0 < chunk ? c.s.BH - bh0 : chunk;
+    e = c.bf16 ? mcs::launch_mass_bf16(c.s, bh0, nbh, Q, K, perm, lse, mass, st)
+               : mcs::launch_mass_f32(c.s, bh0, nbh, Q, K, perm, lse, mass, st);
+    if (e != hipSuccess) return hip_status(e, "mcs_anchor (mass)");
+    e = mcs::launch_topk(c.s, bh0, nbh, mass, idx, st);
+    if (e != hipSuccess) return hip_status(e, "mcs_anchor (top-k)");
+  }
+  e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, R, nullptr, true, st)
+             : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, R, nullptr, true, st);
+  return hip_status(e, "mcs_anchor (sparse)");
+}
+
+mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,
+                           const int32_t* perm, const int32_t* idx, const float* R, void* O,
+                           void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (c.empty) return ok();
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {perm, "perm", false},
+                                 {idx, "idx", false}, {R, "R", true}, {O, "O", false}}))
+    return s;
+  if (O == Q || O == K || O == V || O == (const void*)R)
+    return fail(MCS_ERR_INVALID_ARG, "O aliases an input");
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, (float*)R, O, false, st)
+                              : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, (float*)R, O, false, st);
+  return hip_status(e, "mcs_sparse_attn");
+}
+
+}  // extern "C"

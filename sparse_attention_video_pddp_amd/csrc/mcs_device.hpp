@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, cross-lane exchange, LDS transpose reads, XCD-aware block mapping.
+//
+// Register layouts used throughout (checked on gfx950 hardware):
+//  v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//    A: lane l holds row l%32, k = 8*(l/32) + j  (j = 0..7)
+//    B: lane l holds col l%32, k = 8*(l/32) + j
+//    D: lane l element i is row 8*(i/4) + 4*(l/32) + i%4, col l%32
+//  ds_read_b64_tr_b16: in each group of 16 lanes, lane i element j receives
+//    element i%4 of the 8-byte row addressed by lane 4*j + i/4 of the group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kInf = __builtin_huge_valf();
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane l^32 (exchange of the two wave halves).
+__device__ __forceinline__ float partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane_id() & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposing 8-byte LDS read (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_read_tr(const void* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs in launch order.  Give each
+// XCD a contiguous range of logical work units so that units sharing K/V
+// (neighbouring query tiles or groups of one head) share that XCD's L2.
+// The grid must be launched with 8 * per_xcd blocks; ids beyond the real
+// unit count are returned as-is and must be skipped by the caller.
+__device__ __forceinline__ int xcd_unit(int bid, int per_xcd) { return (bid & 7) * per_xcd + (bid >> 3); }
+
+// Monotone map of a float to an unsigned key (total order, -0 == +0 assumed
+// normalised by the caller).
+__device__ __forceinline__ uint32_t float_order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over one 64-lane wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Raise a kernel's dynamic-LDS limit (host side; done once per kernel).
+inline bool allow_dynamic_lds(const void* kernel, int bytes) {
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  (void)hipGetLastError();
+  return e == hipSuccess;
+}
+
+}  // namespace mcs

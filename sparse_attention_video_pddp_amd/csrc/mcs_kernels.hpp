@@ -1,0 +1,47 @@
+// Internal launch interface between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcs {
+
+// Validated problem, flattened for the launchers.
+struct Shape {
+  int BH;        // B * H
+  int Nq, Nkv, d;
+  int G, k, c;   // group size, kept keys, groups per head
+  float scale;
+  int causal_block, q_offset, iters;
+};
+
+// Dense attention (exact).  O in dtype; lse (natural log) and Ofull (fp32
+// copy of the unrounded output) are optional.
+hipError_t launch_dense_bf16(const Shape& s, const void* Q, const void* K, const void* V, void* O,
+                             float* lse, float* Ofull, hipStream_t st);
+hipError_t launch_dense_f32(const Shape& s, const void* Q, const void* K, const void* V, void* O,
+                            float* lse, float* Ofull, hipStream_t st);
+
+// Per-group exact column mass for heads [bh0, bh0 + nbh): mass[(bh-bh0)*c + g][Nkv].
+hipError_t launch_mass_bf16(const Shape& s, int bh0, int nbh, const void* Q, const void* K,
+                            const int32_t* perm, const float* lse, float* mass, hipStream_t st);
+hipError_t launch_mass_f32(const Shape& s, int bh0, int nbh, const void* Q, const void* K,
+                           const int32_t* perm, const float* lse, float* mass, hipStream_t st);
+
+// Top-k per group row of `mass` (heads [bh0, bh0+nbh)), written to idx[bh][g][k] ascending.
+hipError_t launch_topk(const Shape& s, int bh0, int nbh, const float* mass, int32_t* idx, hipStream_t st);
+
+// Gathered sparse attention.  anchor: R <- R - O_sparse (R holds O_full on
+// entry).  reuse: O <- O_sparse + R (R may be null).
+hipError_t launch_sparse_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
+                              hipStream_t st);
+hipError_t launch_sparse_f32(const Shape& s, const void* Q, const void* K, const void* V,
+                             const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
+                             hipStream_t st);
+
+// PDDP grouping.  ws: int32 tmp [BH*Nq] followed by uint32 keys [BH*Nq].
+size_t pddp_workspace_bytes(const Shape& s);
+hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, void* ws, hipStream_t st);
+
+}  // namespace mcs

@@ -1,0 +1,173 @@
+"""ctypes binding of libmcs.so (the C ABI in include/mcs.h).
+
+Argument marshalling only: every step of the method runs in the library's HIP
+kernels.  PyTorch is used for device memory and the current stream; tensors
+are passed as raw device pointers.  If the library has not been built the
+import of this module still works, but every call raises (there is no CPU
+fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmcs.so")
+
+MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
+MCS_F32, MCS_BF16 = 0, 1
+MCS_WS_GROUP, MCS_WS_ANCHOR = 0, 1
+
+EXPORTED = ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
+            "mcs_status_string", "mcs_last_error", "mcs_version")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nkv", ctypes.c_int32), ("d", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("scale", ctypes.c_float), ("causal_block", ctypes.c_int32),
+                ("q_offset", ctypes.c_int32), ("pddp_iters", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    def __repr__(self) -> str:
+        return "Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+    @property
+    def n_groups(self) -> int:
+        return -(-self.Nq // self.group_size)
+
+
+class MCSError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+_lib = None
+
+
+def _status_name(s: int) -> str:
+    names = {0: "MCS_OK", 1: "MCS_ERR_INVALID_ARG", 2: "MCS_ERR_UNSUPPORTED", 3: "MCS_ERR_WORKSPACE",
+             4: "MCS_ERR_HIP"}
+    return names.get(s, f"status {s}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmcs.so (in-tree build).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_video_pddp_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.mcs_workspace_size.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.mcs_group.argtypes = [P, vp, vp, vp, sz, vp]
+        L.mcs_dense_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.mcs_anchor.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mcs_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        for f in ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn"):
+            getattr(L, f).restype = ctypes.c_int
+        L.mcs_status_string.argtypes = [ctypes.c_int]
+        L.mcs_status_string.restype = ctypes.c_char_p
+        L.mcs_last_error.argtypes = []
+        L.mcs_last_error.restype = ctypes.c_char_p
+        L.mcs_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != MCS_OK:
+        raise MCSError(status, lib().mcs_last_error().decode())
+
+
+def problem(B: int, H: int, Nq: int, Nkv: int, d: int, group_size: int, k: int, scale: Optional[float] = None,
+            causal_block: int = 0, q_offset: int = 0, pddp_iters: int = 32, dtype: str = "bf16") -> Problem:
+    return Problem(B, H, Nq, Nkv, d, group_size, k, 1.0 / math.sqrt(d) if scale is None else scale,
+                   causal_block, q_offset, pddp_iters, {"f32": MCS_F32, "bf16": MCS_BF16}[dtype])
+
+
+def problem_for(w) -> Problem:
+    """Problem of a synthetic workload (``synth.Workload``)."""
+    return problem(w.B, w.H, w.Nq, w.Nkv, w.d, w.group_size, w.k, w.scale, w.causal_block, w.q_offset,
+                   w.pddp_iters, w.dtype)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def workspace_size(p: Problem, kind: int) -> Tuple[int, int]:
+    b, m = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().mcs_workspace_size(ctypes.byref(p), kind, ctypes.byref(b), ctypes.byref(m)))
+    return b.value, m.value
+
+
+def group(p: Problem, Q, perm, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().mcs_group(ctypes.byref(p), _ptr(Q), _ptr(perm), _ptr(ws), nbytes, _stream(stream)))
+
+
+def dense_attn(p: Problem, Q, K, V, O, lse=None, stream=None) -> None:
+    _check(lib().mcs_dense_attn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+                                _stream(stream)))
+
+
+def anchor(p: Problem, Q, K, V, perm, O, idx, R, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().mcs_anchor(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(O), _ptr(idx),
+                            _ptr(R), _ptr(ws), nbytes, _stream(stream)))
+
+
+def sparse_attn(p: Problem, Q, K, V, perm, idx, R, O, stream=None) -> None:
+    _check(lib().mcs_sparse_attn(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(idx), _ptr(R),
+                                 _ptr(O), _stream(stream)))
+
+
+class MCSparseAttention:
+    """Per-layer state of the method across denoising steps: the groups
+    (perm), selections (idx) and residual (R) of the last anchor, held in
+    device tensors, plus the two workspaces.  ``step(Q, K, V, is_anchor)``
+    runs grouping + anchor or the reuse step and returns O."""
+
+    def __init__(self, p: Problem, device="cuda"):
+        import torch
+        self.p = p
+        dt = torch.bfloat16 if p.dtype == MCS_BF16 else torch.float32
+        BH = p.B * p.H
+        self.perm = torch.empty((p.B, p.H, p.Nq), dtype=torch.int32, device=device)
+        self.idx = torch.empty((p.B, p.H, p.n_groups, p.k), dtype=torch.int32, device=device)
+        self.R = torch.empty((p.B, p.H, p.Nq, p.d), dtype=torch.float32, device=device)
+        self.O = torch.empty((p.B, p.H, p.Nq, p.d), dtype=dt, device=device)
+        g, _ = workspace_size(p, MCS_WS_GROUP)
+        a, _ = workspace_size(p, MCS_WS_ANCHOR)
+        self.ws_group = torch.empty(max(g, 1), dtype=torch.uint8, device=device)
+        self.ws_anchor = torch.empty(max(a, 1), dtype=torch.uint8, device=device)
+        self.has_anchor = BH == 0
+
+    def step(self, Q, K, V, is_anchor: bool, stream=None):
+        if is_anchor:
+            group(self.p, Q, self.perm, self.ws_group, stream=stream)
+            anchor(self.p, Q, K, V, self.perm, self.O, self.idx, self.R, self.ws_anchor, stream=stream)
+            self.has_anchor = True
+        else:
+            if not self.has_anchor:
+                raise RuntimeError("a reuse step needs a previous anchor step")
+            sparse_attn(self.p, Q, K, V, self.perm, self.idx, self.R, self.O, stream=stream)
+        return self.O

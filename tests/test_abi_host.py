@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI (not gpu): the library loads, exports every
+symbol the header declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_video_pddp_amd import mcs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "mcs.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mcs_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mcs.lib()
+    names = declared_functions()
+    assert set(names) == set(mcs.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mcs_version() >= 100
+
+
+def test_status_strings():
+    L = mcs.lib()
+    for code, name in enumerate(["MCS_OK", "MCS_ERR_INVALID_ARG", "MCS_ERR_UNSUPPORTED", "MCS_ERR_WORKSPACE",
+                                 "MCS_ERR_HIP"]):
+        assert L.mcs_status_string(code).decode() == name
+
+
+def base(**kw):
+    d = dict(B=1, H=2, Nq=1000, Nkv=1200, d=128, group_size=64, k=60, scale=None, causal_block=0,
+             q_offset=0, pddp_iters=32, dtype="bf16")
+    d.update(kw)
+    return mcs.problem(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), mcs.MCS_ERR_UNSUPPORTED),
+    (dict(group_size=32), mcs.MCS_ERR_UNSUPPORTED),
+    (dict(k=0), mcs.MCS_ERR_INVALID_ARG),
+    (dict(k=1201), mcs.MCS_ERR_INVALID_ARG),
+    (dict(Nkv=0, k=1), mcs.MCS_ERR_INVALID_ARG),
+    (dict(Nq=-1), mcs.MCS_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mcs.MCS_ERR_INVALID_ARG),
+    (dict(scale=0.0), mcs.MCS_ERR_INVALID_ARG),
+    (dict(causal_block=-3), mcs.MCS_ERR_INVALID_ARG),
+    (dict(q_offset=-1), mcs.MCS_ERR_INVALID_ARG),
+    (dict(pddp_iters=5000), mcs.MCS_ERR_INVALID_ARG),
+    (dict(B=300, H=300), mcs.MCS_ERR_UNSUPPORTED),
+])
+def test_bad_problem_is_rejected_before_launch(kw, code):
+    p = base(**kw)
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.dense_attn(p, 16, 16, 16, 32, None, stream=0)
+    assert e.value.status == code
+    b = ctypes.c_size_t()
+    assert mcs.lib().mcs_workspace_size(ctypes.byref(p), 0, ctypes.byref(b), None) == code
+
+
+def test_bad_dtype_rejected():
+    p = base()
+    p.dtype = 7
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.sparse_attn(p, 16, 16, 16, 16, 16, None, 32, stream=0)
+    assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = base()
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.dense_attn(p, None, 16, 16, 32, None, stream=0)
+    assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "Q is NULL" in str(e.value)
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.sparse_attn(p, 16, 16, 16, 16, 16 + 4, None, 32, stream=0)
+    assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "idx" in str(e.value)
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.anchor(p, 16, 16, 16, 16, 32, 48, None, 64, ws_bytes=1 << 30, stream=0)
+    assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "R is NULL" in str(e.value)
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.group(p, 16, None, 64, ws_bytes=1 << 30, stream=0)
+    assert "perm is NULL" in str(e.value)
+
+
+def test_empty_problem_is_a_noop_without_pointers():
+    p = base(Nq=0)
+    mcs.dense_attn(p, None, None, None, None, None, stream=0)
+    mcs.sparse_attn(p, None, None, None, None, None, None, None, stream=0)
+    assert mcs.workspace_size(p, mcs.MCS_WS_ANCHOR) == (0, 0)
+    p = base(H=0)
+    mcs.group(p, None, None, None, ws_bytes=0, stream=0)
+
+
+def test_workspace_sizes():
+    p = base()
+    g, gmin = mcs.workspace_size(p, mcs.MCS_WS_GROUP)
+    assert g == gmin and g >= 2 * 4 * 2 * 1000
+    a, amin = mcs.workspace_size(p, mcs.MCS_WS_ANCHOR)
+    c = -(-1000 // 64)
+    assert amin >= 4 * 2 * 1000 + 4 * c * 1200
+    assert a >= amin + 4 * c * 1200
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.workspace_size(p, 9)
+    assert e.value.status == mcs.MCS_ERR_INVALID_ARG

@@ -1,0 +1,163 @@
+"""GPU parity at oracle-sized workloads (all heads, all groups, all rows).
+
+Each workload is a scaled-down grid of one of the five benchmark workloads,
+large enough to span several K/V tiles with a ragged tail, several PDDP
+levels and a short last group.  The anchor runs on step 0, the reuse step on
+step 1 (drifted inputs).  Every stage is compared with the fp64 oracle as
+described in tests/parity.py.
+"""
+import numpy as np
+import pytest
+
+from sparse_attention_video_pddp_amd import synth
+from tests.parity import assert_reports, check_head
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # fp32 smoke workload at its real size: 1024 tokens, G=64, k=103
+    "tiny": synth.get("tiny"),
+    # bidirectional, bf16: 720 tokens -> 12 groups (last 16), k=144 (3 tiles, last ragged)
+    "bidir_small": synth.get("bidir5").with_(name="bidir_small", H=2, grid=(3, 12, 20), keep_permille=200),
+    # frame-causal query chunk: 900 keys in frames of 150, queries = last 2 frames (300 -> 5 groups, last 44)
+    "causal_small": synth.get("causal").with_(name="causal_small", H=2, grid=(6, 10, 15), q_frames=(4, 6),
+                                              causal_block=150, keep_permille=100),
+    # G=128, temperature 3/sqrt(d): 1200 tokens -> 10 groups (last 48), k=360
+    "large_small": synth.get("large").with_(name="large_small", H=2, grid=(4, 15, 20), keep_permille=300),
+    # 3D-local field generator, d=64, G=128: 2048 tokens -> 16 groups, k=205
+    "stress_small": synth.get("stress").with_(name="stress_small", H=2, grid=(8, 16, 16), keep_permille=100),
+}
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workload_parity(cuda, name):
+    from tests.gpu_runner import log, run_anchor_reuse
+    w = SMALL[name]
+    heads = [(0, h) for h in range(w.H)]
+    cases = run_anchor_reuse(w, heads)
+    for bh, case in cases.items():
+        reps = check_head(case, w.group_size, w.k, w.scale, w.causal_block, w.q_offset, w.pddp_iters)
+        for r in reps:
+            log(f"  {name} head {bh}: {r}")
+        assert_reports(reps, f"{name} head {bh}")
+
+
+def test_dense_attn_matches_oracle_with_lse(cuda):
+    import torch
+    from oracle.mcs_oracle import dense_attention
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    for w in (SMALL["causal_small"], SMALL["stress_small"], SMALL["tiny"]):
+        p = mcs.problem_for(w)
+        (Q, K, V), host = device_inputs(w, 0, keep_heads=[(0, 1)])
+        O = torch.empty_like(Q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+        mcs.dense_attn(p, Q, K, V, O, lse)
+        torch.cuda.synchronize()
+        q, k, v = (x.astype(np.float64) for x in host[(0, 1)])
+        Oo, lo = dense_attention(q, k, v, w.scale, w.causal_block, w.q_offset)
+        vmax = np.abs(v).max()
+        d = np.abs(O[0, 1].float().cpu().numpy() - Oo)
+        assert d.max() <= 1e-2 * vmax and d.mean() <= 1e-3 * vmax, (w.name, d.max(), d.mean())
+        dl = np.abs(lse[0, 1].cpu().numpy() - lo)
+        assert dl.max() <= 1e-4 * max(1.0, np.abs(lo).max()), (w.name, dl.max())
+
+
+def _state(w):
+    from sparse_attention_video_pddp_amd import mcs
+    return mcs.MCSparseAttention(mcs.problem_for(w))
+
+
+def test_full_keep_sparse_equals_dense(cuda):
+    """keep 100%: every group selects every key, so the GPU's sparse kernel
+    (without R) must reproduce the GPU's dense kernel."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    for base in ("bidir_small", "causal_small"):
+        w = SMALL[base].with_(keep_permille=1000)
+        p = mcs.problem_for(w)
+        (Q, K, V), _ = device_inputs(w, 0)
+        st = _state(w)
+        st.step(Q, K, V, True)
+        assert torch.equal(st.idx[0, 0, 0], torch.arange(w.Nkv, dtype=torch.int32, device="cuda"))
+        Od = torch.empty_like(Q)
+        mcs.dense_attn(p, Q, K, V, Od)
+        Os = torch.empty_like(Q)
+        mcs.sparse_attn(p, Q, K, V, st.perm, st.idx, None, Os)
+        torch.cuda.synchronize()
+        vmax = V.float().abs().max().item()
+        d = (Os.float() - Od.float()).abs()
+        assert d.max().item() <= 1e-2 * vmax and d.mean().item() <= 1e-3 * vmax, (base, d.max().item())
+        assert st.R.abs().max().item() <= 1e-2 * vmax
+
+
+def test_zero_drift_reuse_returns_anchor_output(cuda):
+    import torch
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    for base in ("bidir_small", "causal_small", "stress_small", "tiny"):
+        w = SMALL[base]
+        (Q, K, V), _ = device_inputs(w, 0)
+        st = _state(w)
+        Oa = st.step(Q, K, V, True).clone()
+        Or = st.step(Q, K, V, False)
+        torch.cuda.synchronize()
+        vmax = V.float().abs().max().item()
+        d = (Or.float() - Oa.float()).abs().max().item()
+        assert d <= 1e-2 * vmax, (base, d)
+        # R absorbs the discarded tail: reuse output equals the anchor's dense output to rounding
+        assert d <= 2.0 ** -7 * max(1.0, Oa.float().abs().max().item()), (base, d)
+
+
+def test_runs_are_bitwise_deterministic(cuda):
+    import torch
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    w = SMALL["large_small"]
+    (Q, K, V), _ = device_inputs(w, 0)
+    outs = []
+    for _ in range(2):
+        st = _state(w)
+        O = st.step(Q, K, V, True).clone()
+        O2 = st.step(Q, K, V, False).clone()
+        torch.cuda.synchronize()
+        outs.append((st.perm.clone(), st.idx.clone(), st.R.clone(), O, O2))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_empty_query_set_is_a_noop(cuda):
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    p = mcs.problem(1, 2, 0, 128, 64, 64, 10)
+    x = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16, device="cuda")
+    mcs.dense_attn(p, x, x, x, torch.empty_like(x))
+    mcs.sparse_attn(p, x, x, x, torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    torch.zeros(1, dtype=torch.int32, device="cuda"), None, torch.empty_like(x))
+    torch.cuda.synchronize()
+
+
+def test_single_group_and_single_key_edges(cuda):
+    """Nq < G (one group, no PDDP split) and k = 1 (every query returns its
+    group's one selected value row)."""
+    import torch
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    w = SMALL["bidir_small"].with_(grid=(1, 5, 10), keep_permille=1)   # 50 tokens, k = 1
+    assert w.k == 1 and w.n_groups == 1
+    (Q, K, V), host = device_inputs(w, 0, keep_heads=[(0, 0)])
+    st = _state(w)
+    st.step(Q, K, V, True)
+    Os = st.step(Q, K, V, False)
+    torch.cuda.synchronize()
+    assert torch.equal(st.perm[0, 0], torch.arange(50, dtype=torch.int32, device="cuda"))
+    j = int(st.idx[0, 0, 0, 0])
+    # sparse part of every row is V[j]; reuse O = V[j] + R = O_full (to rounding)
+    R = st.R[0, 0]
+    sp = (Os[0, 0].float() - R)
+    assert (sp - V[0, 0, j].float()).abs().max().item() <= 2e-2
