@@ -1,0 +1,267 @@
+"""Benchmark of the MC-Sparse hot path on one MI355X.
+
+One bench step is one anchor period of the denoising schedule over the whole
+hot path: PDDP grouping + anchor (exact dense attention, per-group column
+mass, top-k, anchor sparse attention and residual) on the anchor step's
+inputs, then the reuse steps (gathered sparse attention + R) on the following
+steps' drifted inputs.  All inputs are generated up front and resident in HBM
+before the timed region.  Every library call is bracketed by HIP events on
+the stream the library launches on; the metric is the reuse step
+(mcs_sparse_attn).  The library's own exact attention (mcs_dense_attn) is
+timed on the same rotating inputs as the comparator.
+
+Prints one JSON line (rank 0).  See --help.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/call + effective TFLOP/s (% bf16 MFMA peak) of sparse reuse step, N=32760"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10, help="timed anchor periods")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed anchor periods")
+    ap.add_argument("--config", default="bidir5", help="workload name (synth.CONFIGS)")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for profiler counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "mcs_device.hpp"):
+        with open(os.path.join(ROOT, "sparse_attention_video_pddp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, config: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel, {}).get(config)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def reuse_bytes_per_launch(w) -> float:
+    """Algorithmic bytes of one mcs_sparse_attn call: per (b,h,group) the k
+    gathered K and V rows (bf16), the group's Q rows (bf16), R rows (fp32),
+    O rows (bf16) and the k indices (int32)."""
+    e = 2 if w.dtype == "bf16" else 4
+    BH = w.B * w.H
+    return BH * (w.n_groups * (2 * w.k * w.d * e + 4 * w.k) + w.Nq * w.d * (e + 4 + e))
+
+
+def dense_flops(w) -> float:
+    """4*d per visible (query, key) pair (QK^T and PV)."""
+    if w.causal_block == 0:
+        pairs = w.Nq * w.Nkv
+    else:
+        pairs = 0
+        for i in range(w.Nq):
+            pairs += min(w.Nkv, ((w.q_offset + i) // w.causal_block + 1) * w.causal_block)
+    return 4.0 * w.d * pairs * w.B * w.H
+
+
+def reuse_flops(w) -> float:
+    return 4.0 * w.d * w.Nq * w.k * w.B * w.H
+
+
+def cpu_baseline(w, host0, host1, nheads: int):
+    """The oracle as it stands, on a bounded sample of heads: its own anchor
+    (PDDP, dense attention, column mass, top-k, residual) prepares each
+    sampled head, then its reuse step (the metric's operation) is timed."""
+    import numpy as np
+    from oracle.mcs_oracle import anchor_step, reuse_step
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    heads = sorted(host0)[:nheads]
+    t_anchor = t_reuse = 0.0
+    for bh in heads:
+        q0, k0, v0 = (x.astype(np.float64) for x in host0[bh])
+        q1, k1, v1 = (x.astype(np.float64) for x in host1[bh])
+        t0 = time.perf_counter()
+        a = anchor_step(q0, k0, v0, w.group_size, w.k, w.scale, w.causal_block, w.q_offset, w.pddp_iters)
+        t1 = time.perf_counter()
+        reuse_step(q1, k1, v1, a["perm"], a["idx"], a["R"], w.group_size, w.scale, w.causal_block, w.q_offset)
+        t2 = time.perf_counter()
+        t_anchor += t1 - t0
+        t_reuse += t2 - t1
+    per_head = dense_flops(w) / (w.B * w.H)
+    n = len(heads)
+    return {"value": round(per_head * n / t_reuse / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.B * w.H} heads of {w.name}: the oracle's reuse step (numpy fp64 gathered "
+                      f"sparse attention + R, on the oracle's own anchor of step 0) on step-1 inputs; "
+                      f"{t_reuse:.1f} s timed ({t_reuse / n * 1e3:.0f} ms per head); dense-equivalent FLOPs",
+            "reuse_ms_per_call_extrapolated": round(t_reuse / n * w.B * w.H * 1e3, 1),
+            "anchor_ms_per_call_extrapolated": round(t_anchor / n * w.B * w.H * 1e3, 1),
+            "cpu": platform.processor() or platform.machine(), "numpy": np.__version__}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every box here has one MI355X and the method's "
+              "kernels run on one GPU's share; --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from sparse_attention_video_pddp_amd import mcs, synth
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+
+    w = synth.get(args.config)
+    p = mcs.problem_for(w)
+    A = min(w.anchor_every, w.steps)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    print(f"[bench] {w.name}: {p}", file=sys.stderr, flush=True)
+    keep = [(0, h) for h in range(min(args.cpu_heads, w.H))] if not args.no_cpu_baseline else []
+    step_in, host = [], {}
+    for s in range(A):
+        (Q, K, V), hs = device_inputs(w, s, keep_heads=keep)
+        step_in.append((Q, K, V))
+        host[s] = hs
+    print(f"[bench] inputs resident: {A} steps x {3 * Q.numel() * Q.element_size() / 1e9:.2f} GB",
+          file=sys.stderr, flush=True)
+    st = mcs.MCSparseAttention(p)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def period(record):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        mcs.group(p, step_in[0][0], st.perm, st.ws_group, stream=stream)
+        e1.record(stream)
+        mcs.anchor(p, *step_in[0], st.perm, st.O, st.idx, st.R, st.ws_anchor, stream=stream)
+        e2.record(stream)
+        re = []
+        for s in range(1, A):
+            a, b = ev(), ev()
+            a.record(stream)
+            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
+            b.record(stream)
+            re.append((a, b))
+        if record is not None:
+            record.append(((e0, e1), (e1, e2), re))
+
+    for _ in range(args.warmup):
+        period(None)
+    torch.cuda.synchronize()
+    rec = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        period(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    group_ms = [a.elapsed_time(b) for (a, b), _, _ in rec]
+    anchor_ms = [a.elapsed_time(b) for _, (a, b), _ in rec]
+    reuse_ms = [a.elapsed_time(b) for _, _, re in rec for (a, b) in re]
+
+    # comparator: the library's exact attention, same rotating inputs and count
+    Od = torch.empty_like(st.O)
+    for s in range(1, A):
+        mcs.dense_attn(p, *step_in[s], Od, stream=stream)
+    torch.cuda.synchronize()
+    dense_ms = []
+    for i in range(max(1, len(reuse_ms) // 2)):
+        s = 1 + i % (A - 1)
+        a, b = ev(), ev()
+        a.record(stream)
+        mcs.dense_attn(p, *step_in[s], Od, stream=stream)
+        b.record(stream)
+        dense_ms.append((a, b))
+    torch.cuda.synchronize()
+    dense_ms = [a.elapsed_time(b) for a, b in dense_ms]
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    f_dense, f_reuse = dense_flops(w), reuse_flops(w)
+    r_mean = statistics.fmean(reuse_ms)
+    d_mean = statistics.fmean(dense_ms)
+    value = f_dense / (r_mean * 1e-3) / 1e12
+    rbytes = reuse_bytes_per_launch(w)
+    traffic = load_traffic("sparse_bf16_kernel", w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: full bidirectional 3D attention over a {w.grid[0]}x{w.grid[1]}x"
+                               f"{w.grid[2]} = {w.Nkv}-token video latent, B={w.B}, H={w.H}, d={w.d}, "
+                               f"{w.dtype}, PDDP groups of {w.group_size}, keep {w.keep_permille / 10:g}% "
+                               f"(k={w.k}), anchor every {A} steps, drift {w.drift} N(0,1) per step",
+                   "B": w.B, "H": w.H, "N": w.Nkv, "d": w.d, "group_size": w.group_size, "k": w.k,
+                   "anchor_every": A},
+        "step": f"one anchor period: mcs_group + mcs_anchor on step 0, mcs_sparse_attn on steps 1..{A - 1}",
+        "reuse_ms_per_call": round(r_mean, 4),
+        "reuse_ms_median": round(statistics.median(reuse_ms), 4),
+        "reuse_ms_min": round(min(reuse_ms), 4),
+        "reuse_effective_tflops_dense_equiv": round(value, 2),
+        "reuse_effective_frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "reuse_executed_tflops": round(f_reuse / (r_mean * 1e-3) / 1e12, 2),
+        "reuse_executed_frac_bf16_peak": round(f_reuse / (r_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dense_ms_per_call": round(d_mean, 4),
+        "dense_tflops": round(f_dense / (d_mean * 1e-3) / 1e12, 2),
+        "dense_frac_bf16_peak": round(f_dense / (d_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "speedup_reuse_vs_dense": round(d_mean / r_mean, 2),
+        "group_ms": round(statistics.fmean(group_ms), 4),
+        "anchor_ms": round(statistics.fmean(anchor_ms), 4),
+        "period_effective_tflops_dense_equiv": round(A * f_dense / (wall / args.steps) / 1e12, 2),
+        "roofline": {"kernel": "sparse_bf16_kernel (mcs_sparse_attn, reuse step)", "bound": "hbm",
+                     "achieved": round(rbytes / (r_mean * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(rbytes / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": rbytes,
+                     "mfma_view_tflops": round(f_reuse / (r_mean * 1e-3) / 1e12, 2)},
+        "roofline_dense": {"kernel": "dense_bf16_kernel (mcs_dense_attn)", "bound": "mfma",
+                           "achieved": round(f_dense / (d_mean * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(f_dense / (d_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "traffic": load_traffic("dense_bf16_kernel", w.name)},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, host[0], host[1], args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

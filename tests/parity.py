@@ -1,14 +1,17 @@
 """Staged parity checks of GPU results against the fp64 oracle.
 
-Each stage is checked on the exact inputs the GPU consumed, so a legitimate
-near-tie in one stage cannot cascade into the next:
-  * groups: perm must be a valid grouping and, node by node, each split must
-    equal the oracle's split of the GPU's parent set, except tokens whose
-    oracle projection lies within 1e-5 * max|p| of the split point;
-  * top-k: on the GPU's groups, the selected set must equal the oracle's,
-    except keys whose oracle mass is within 1e-5 relative of the k-th mass;
-  * outputs (O_full, R, reuse O): on the GPU's groups and selections,
-    max|dO| <= 1e-2 * max|V| and mean|dO| <= 1e-3 * max|V|.
+The oracle runs end to end on its own results (its own PDDP grouping, its own
+top-k selections).  fp32 on the GPU and fp64 in the oracle may legitimately
+decide a near-tie differently; only then is the GPU's choice validated
+instead of compared, and the later stages of that group are computed on the
+validated choice, so one near-tie cannot cascade:
+  * groups: perm must equal the oracle's grouping, or else be a valid grouping
+    whose every split equals the oracle's split of the GPU's parent set except
+    tokens whose oracle projection lies within 1e-5 * max|p| of the split point;
+  * top-k: each group's selection must equal the oracle's, or else differ
+    only in keys whose oracle mass is within 1e-5 relative of the k-th mass;
+  * outputs (O_full, R, reuse O): max|dO| <= 1e-2 * max|V| and
+    mean|dO| <= 1e-3 * max|V| (bf16 inputs, fp32 accumulation).
 """
 from __future__ import annotations
 
@@ -124,37 +127,63 @@ def check_head(case: HeadCase, G: int, k: int, scale: float, causal_block: int, 
                groups: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
                max_nodes: Optional[int] = None) -> List[StageReport]:
     """Staged parity of one head.  ``groups``/``rows`` restrict the checks to
-    sampled groups and dense rows (full-size workloads); None = all."""
-    reps = [check_groups_nodewise(case.Q0, case.perm, G, iters, max_nodes)]
+    sampled groups and dense rows (full-size workloads); None = all.
+
+    The oracle runs on its own results: its own PDDP grouping and its own
+    top-k selections.  Only where the GPU's result legitimately differs (a
+    split or selection decided by a near-tie, see the module docstring) is the
+    GPU's choice validated instead, and the later stages of that group are then
+    computed on the validated choice; the reports count such cases.
+    """
+    reps = []
     Nq = case.Q0.shape[0]
     sl = orc.group_slices(Nq, G)
     gsel = list(range(len(sl))) if groups is None else list(groups)
-    perm = np.asarray(case.perm, np.int64)
+    perm_gpu = np.asarray(case.perm, np.int64)
+    perm_o = orc.pddp_groups(case.Q0, G, iters)
+    if np.array_equal(perm_o, perm_gpu):
+        reps.append(StageReport("groups", True, "bit-exact with the oracle's PDDP grouping"))
+        perm_ref = perm_o
+    else:
+        r = check_groups_nodewise(case.Q0, perm_gpu, G, iters, max_nodes)
+        reps.append(StageReport("groups", r.ok, "differs from the oracle's grouping; validated split by "
+                                                "split: " + r.detail))
+        perm_ref = perm_gpu
     # dense rows (anchor inputs)
     drows = np.arange(Nq) if rows is None else np.asarray(rows, np.int64)
-    Od, lse_rows = orc.dense_attention(case.Q0, case.K0, case.V0, scale, causal_block, q_offset, rows=drows)
+    Od, _ = orc.dense_attention(case.Q0, case.K0, case.V0, scale, causal_block, q_offset, rows=drows)
     vmax0 = float(np.abs(case.V0).max())
     reps.append(compare("O_full (dense rows)", case.O_full[drows], Od, vmax0))
-    # top-k on the GPU's groups, with the oracle's own lse
-    msgs = []
+    # top-k: the oracle's own selection per group
+    msgs, exact, band = [], 0, 0
+    idx_ref = np.zeros((len(sl), k), np.int64)
+    member_rows = np.concatenate([perm_ref[sl[g]] for g in gsel])
+    Ofull_m, lse_m = orc.dense_attention(case.Q0, case.K0, case.V0, scale, causal_block, q_offset,
+                                         rows=member_rows)
+    lse_full = np.full(Nq, np.nan)
+    lse_full[member_rows] = lse_m
     for g in gsel:
-        members = perm[sl[g]]
-        _, lse_m = orc.dense_attention(case.Q0, case.K0, case.V0, scale, causal_block, q_offset, rows=members)
-        lse_full = np.full(Nq, np.nan)
-        lse_full[members] = lse_m
+        members = perm_ref[sl[g]]
         m = orc.column_mass(case.Q0, case.K0, lse_full, members, scale, causal_block, q_offset)
+        own = orc.topk_select(m, k)
+        if np.array_equal(own, np.asarray(case.idx[g], np.int64)):
+            exact += 1
+            idx_ref[g] = own
+            continue
         e = check_topk(m, case.idx[g], k, g)
         if e:
             msgs.append(e)
-    reps.append(StageReport("top-k", not msgs, msgs[0] if msgs else f"{len(gsel)} groups equal up to near-ties"))
-    # residual and reuse on the GPU's groups and selections
-    member_rows = np.concatenate([perm[sl[g]] for g in gsel])
-    Ofull_m, _ = orc.dense_attention(case.Q0, case.K0, case.V0, scale, causal_block, q_offset, rows=member_rows)
-    Osp0 = orc.sparse_attention(case.Q0, case.K0, case.V0, perm, case.idx, G, scale, causal_block, q_offset,
+        else:
+            band += 1
+            idx_ref[g] = np.asarray(case.idx[g], np.int64)
+    reps.append(StageReport("top-k", not msgs, msgs[0] if msgs else
+                            f"{exact} groups bit-exact, {band} equal up to near-ties"))
+    # residual and reuse on the reference groups and selections
+    Osp0 = orc.sparse_attention(case.Q0, case.K0, case.V0, perm_ref, idx_ref, G, scale, causal_block, q_offset,
                                 groups=gsel)[member_rows]
     R_ora = Ofull_m - Osp0
     reps.append(compare("R (anchor residual)", case.R[member_rows], R_ora, vmax0))
-    Osp1 = orc.sparse_attention(case.Q1, case.K1, case.V1, perm, case.idx, G, scale, causal_block, q_offset,
+    Osp1 = orc.sparse_attention(case.Q1, case.K1, case.V1, perm_ref, idx_ref, G, scale, causal_block, q_offset,
                                 groups=gsel)[member_rows]
     reps.append(compare("O (reuse step)", case.O_reuse[member_rows], Osp1 + R_ora,
                         float(np.abs(case.V1).max())))
