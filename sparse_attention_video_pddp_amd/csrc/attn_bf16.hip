@@ -21,6 +21,8 @@
 namespace mcs {
 namespace {
 
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
 template <int D>
 struct Tile {
   static constexpr int KS = D + 8;   // K row stride (elements)
@@ -108,8 +110,11 @@ struct Flash {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, partner32(mx));
-    const float m_new = fmaxf(m_run, mx * c);
+    mx = fmaxf(mx, partner32(mx)) * c;
+    // Lazy rescaling: keep the reference maximum unless this tile exceeds it
+    // by more than 2^8 (probabilities stay <= 256, far from fp32/bf16 limits;
+    // the final normalisation by the row sum makes the result exact).
+    const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
     const float m_ref = (m_new == -kInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_ref);
     m_run = m_new;
@@ -148,7 +153,7 @@ struct Flash {
   // 1 / row sum (0 for a row with no visible key) and the natural-log lse.
   __device__ __forceinline__ float finish(float& lse) {
     const float lt = l_run + partner32(l_run);
-    lse = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -kInf;
+    lse = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -kInf;
     return lt > 0.f ? 1.f / lt : 0.f;
   }
 };
@@ -206,7 +211,7 @@ struct DenseParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dense_bf16_kernel(DenseParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dense_bf16_kernel(DenseParams p) {
   constexpr int NT = 256, QR = 128;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * Tile<D>::KS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[64 * Tile<D>::VS];
@@ -264,7 +269,7 @@ struct SparseParams {
 };
 
 template <int D, int G, bool IDX_LDS>
-__global__ __launch_bounds__(2 * G) void sparse_bf16_kernel(SparseParams p) {
+__global__ __launch_bounds__(2 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_bf16_kernel(SparseParams p) {
   constexpr int NW = G / 32, NT = NW * 64;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * Tile<D>::KS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[64 * Tile<D>::VS];
