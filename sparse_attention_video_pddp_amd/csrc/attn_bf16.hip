@@ -1,10 +1,10 @@
-// bf16 attention kernels on gfx950 MFMA: exact dense attention, the anchor's
-// per-group column mass, and gathered sparse attention with the residual.
+// bf16 attention kernels on gfx950 MFMA: exact dense attention and the
+// anchor's per-group column mass.
 //
 // Method: MC-Sparse review (blog.secrett2633.cloud), section "3. Method & Key
-// Results": exact scores at an anchor step, token-level KV selection per query
-// group, reuse of the selection on later steps with the residual
-// R = O_full - O_sparse added back.
+// Results": exact scores at the anchor step, from which each query group's
+// token-level KV selection is made.  (The gathered sparse attention of the
+// reuse step is in sparse_bf16.hip.)
 //
 // Shared structure.  One wave owns 32 query rows.  K/V tiles of 64 keys are
 // staged in LDS (row-major; K rows padded so 16-lane 16-byte reads hit
@@ -255,98 +255,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Gathered sparse attention: one workgroup per (head, group), G/32 waves.
-// ---------------------------------------------------------------------------
-struct SparseParams {
-  const __bf16 *Q, *K, *V;
-  const int32_t *perm, *idx;
-  float* R;
-  __bf16* O;
-  int Nq, Nkv, k, c, n_units, per_xcd;
-  float c_log2;
-  int causal_block, q_offset;
-  int anchor;
-};
-
-template <int D, int G, bool IDX_LDS>
-__global__ __launch_bounds__(2 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_bf16_kernel(SparseParams p) {
-  constexpr int NW = G / 32, NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * Tile<D>::KS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[64 * Tile<D>::VS];
-  __shared__ int s_kmax[NW];
-  extern __shared__ int s_idx[];
-  const int unit = xcd_unit(blockIdx.x, p.per_xcd);
-  if (unit >= p.n_units) return;
-  const int bh = unit / p.c, g = unit - bh * p.c;
-  const int w = wave_id(), l = lane_id(), n = l & 31;
-  const int32_t* gidx = p.idx + ((size_t)bh * p.c + g) * p.k;
-  const int* sel = gidx;
-  if constexpr (IDX_LDS) {
-    for (int i = threadIdx.x; i < p.k; i += NT) s_idx[i] = gidx[i];
-    __syncthreads();
-    sel = s_idx;
-  }
-  const int gsize = min(G, p.Nq - g * G);
-  const int qloc = w * 32 + n;
-  const bool qv = qloc < gsize;
-  const int32_t* gperm = p.perm + (size_t)bh * p.Nq + (size_t)g * G;
-  // caller data is not validated on the device; clamping keeps every access in bounds
-  const int qrow = min(max(gperm[qv ? qloc : 0], 0), p.Nq - 1);
-  int vcount = qv ? p.k : 0;
-  if (qv && p.causal_block) {
-    // selected keys are ascending: the visible ones are a prefix of the list
-    const int lim = visible_limit(qrow, p.causal_block, p.q_offset, p.Nkv);
-    int lo = 0, hi = p.k;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (sel[mid] < lim) lo = mid + 1; else hi = mid;
-    }
-    vcount = lo;
-  }
-  int vm = vcount;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) vm = max(vm, __shfl_xor(vm, o, 64));
-  if (l == 0) s_kmax[w] = vm;
-  __syncthreads();
-  int kmax = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) kmax = max(kmax, s_kmax[i]);
-  const int ntiles = (kmax + 63) / 64;
-  const __bf16* Kh = p.K + (size_t)bh * p.Nkv * D;
-  const __bf16* Vh = p.V + (size_t)bh * p.Nkv * D;
-  Flash<D> st;
-  st.init(p.Q + ((size_t)bh * p.Nq + qrow) * D, qv);
-  TileStage<D, NT, true> stage;
-  const int last = p.k - 1, klast = p.Nkv - 1;
-  if (ntiles > 0) {
-    stage.load(Kh, Vh, [&](int r) { return min(max(sel[min(r, last)], 0), klast); });
-    stage.store(Ks, Vs);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int base = t * 64;
-    const bool more = t + 1 < ntiles;
-    if (more) stage.load(Kh, Vh, [&](int r) { return min(max(sel[min(base + 64 + r, last)], 0), klast); });
-    st.tile(Ks, Vs, vcount - base, p.c_log2);
-    __syncthreads();
-    if (more) {
-      stage.store(Ks, Vs);
-      __syncthreads();
-    }
-  }
-  float lse;
-  const float inv = st.finish(lse);
-  if (qv) {
-    const size_t row = (size_t)bh * p.Nq + qrow;
-    if (p.anchor) {
-      store_row_f32<D>(p.R + row * D, st, inv, true);
-    } else {
-      store_row_bf16<D>(p.O + row * D, st, inv, p.R ? p.R + row * D : nullptr);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Anchor column mass: m_g[j] = sum_{i in g} exp(scale*<q_i,k_j> - lse_i).
 // 128 queries (4 waves) per workgroup = 128/G groups.  Scores are formed as
 // S = Q K^T here so that a lane holds one key column: its mass over the
@@ -474,36 +382,6 @@ hipError_t launch_dense_bf16(const Shape& s, const void* Q, const void* K, const
   grid_for(p, s.BH * p.n_qtiles, grid);
   if (s.d == 128) hipLaunchKernelGGL(dense_bf16_kernel<128>, grid, dim3(256), 0, st, p);
   else hipLaunchKernelGGL(dense_bf16_kernel<64>, grid, dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_sparse_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
-                              hipStream_t st) {
-  SparseParams p;
-  p.Q = (const __bf16*)Q; p.K = (const __bf16*)K; p.V = (const __bf16*)V;
-  p.perm = perm; p.idx = idx; p.R = R; p.O = (__bf16*)O;
-  p.Nq = s.Nq; p.Nkv = s.Nkv; p.k = s.k; p.c = s.c;
-  p.c_log2 = s.scale * kLog2e; p.causal_block = s.causal_block; p.q_offset = s.q_offset;
-  p.anchor = anchor ? 1 : 0;
-  dim3 grid;
-  grid_for(p, s.BH * s.c, grid);
-  const bool lds = s.k <= 8192;
-  const size_t dyn = lds ? (size_t)s.k * sizeof(int) : 0;
-  const dim3 block(2 * s.G);
-#define MCS_SPARSE(D_, G_)                                                                     \
-  if (lds) {                                                                                   \
-    static const bool attr = allow_dynamic_lds((const void*)sparse_bf16_kernel<D_, G_, true>, 8192 * 4); \
-    (void)attr;                                                                                \
-    hipLaunchKernelGGL((sparse_bf16_kernel<D_, G_, true>), grid, block, dyn, st, p);           \
-  } else {                                                                                     \
-    hipLaunchKernelGGL((sparse_bf16_kernel<D_, G_, false>), grid, block, 0, st, p);            \
-  }
-  if (s.d == 128 && s.G == 64) { MCS_SPARSE(128, 64) }
-  else if (s.d == 128) { MCS_SPARSE(128, 128) }
-  else if (s.G == 64) { MCS_SPARSE(64, 64) }
-  else { MCS_SPARSE(64, 128) }
-#undef MCS_SPARSE
   return hipGetLastError();
 }
 
