@@ -99,11 +99,12 @@ struct Flash {
       }
     }
     if (lim < 64) {
+      const int lh = lim - 4 * h;  // element i of block kb is key kb*32 + 8*(i/4) + 4*h + i%4
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= lim) s[kb][i] = -kInf;
+          if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lh) s[kb][i] = -kInf;
     }
     float mx = -kInf;
 #pragma unroll

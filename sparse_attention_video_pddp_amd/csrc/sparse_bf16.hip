@@ -162,11 +162,12 @@ void sparse_ring_kernel(Params p) {
       const bf16x8 a = *(const bf16x8*)(Ks + n * D + ((cch ^ swz<D>(n)) * 8));
       s = mfma_32x32x16(a, qb[ks], s);
     }
-    const int lim = vcount - t * C::TK;
-    if (lim < C::TK) {
+    // element i holds key 8*(i/4) + 4*h + i%4 of the tile; mask keys >= lim
+    const int lim = vcount - t * C::TK - 4 * h;
+    if (lim < C::TK - 4) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (8 * (i >> 2) + 4 * h + (i & 3) >= lim) s[i] = -kInf;
+        if (8 * (i >> 2) + (i & 3) >= lim) s[i] = -kInf;
     }
     float mx = -kInf;
 #pragma unroll
