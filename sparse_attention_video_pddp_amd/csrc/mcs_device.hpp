@@ -79,9 +79,33 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// fp64 value of another lane by a DPP pattern (both 32-bit halves moved).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+__device__ __forceinline__ double partner32_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+  auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  const bool up = lane_id() & 32;
+  const unsigned l = up ? lo[0] : lo[1], h = up ? hi[0] : hi[1];
+  return __longlong_as_double((long long)(((unsigned long long)h << 32) | l));
+}
+
+// Sum over the 64 lanes, returned in every lane: DPP within rows of 16
+// (quad swaps, half-row and row mirrors), then the row pairs and the halves.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16, 64);
+  v += partner32_f64(v);
   return v;
 }
 

@@ -2,167 +2,257 @@
 // section 3: similar queries are packed into equal-size, tile-aligned groups
 // by Principal Direction Divisive Partitioning).
 //
-// The tree is processed level by level; at each level one workgroup owns one
-// node, i.e. one contiguous range perm[start, start+n) of a head (groups are
-// numbered depth-first, so every node stays contiguous).  For a node holding
-// c >= 2 groups the workgroup
-//   1. forms S = sum x and the raw scatter sum x x^T over the node's query
-//      rows: bf16 rows through v_mfma_f32_32x32x16_bf16 (exact products,
-//      fp32 accumulation over 64-row chunks, fp64 across chunks), fp32 rows
-//      with fp64 FMA;
-//   2. centres it, C = sum x x^T - S S^T / n (fp64), and runs the fixed-step
-//      power iteration v <- C v / ||C v|| from v0 = 1/sqrt(d) in fp64
-//      (a zero product keeps v);
-//   3. projects p_i = (x_i - mean) . v in fp64 and stores an order key of
-//      float(p_i);
-//   4. radix-selects the (floor(c/2)*G)-th smallest key and stably partitions
-//      the members (key, then position = original index, since members are
-//      kept ascending) into the left and right child ranges.
-// Wave w of the workgroup holds column block w of C in the MFMA output layout
-// (lane: one column, 16 rows per 32-row block), so C v needs only an in-lane
-// sum and one half-wave exchange (C is symmetric).
-#include "mcs_device.hpp"
+// The tree is processed level by level.  Groups are numbered depth-first, so
+// every node is one contiguous range perm[start, start+n) of its head, and
+// the node's shape (start, n, c groups) follows from its slot number alone.
+// For a node with c >= 2 groups:
+//   1. S = sum x and the raw scatter sum x x^T over the node's rows: bf16
+//      rows through v_mfma_f32_32x32x16_bf16 (exact products, fp32 sums over
+//      64-row tiles, fp64 across tiles), fp32 rows with fp64 FMAs;
+//   2. C = sum x x^T - S S^T / n (fp64) and the fixed-step power iteration
+//      v <- C v / ||C v|| from v0 = 1/sqrt(d) in fp64 (a zero product keeps v);
+//   3. projections p_i = x_i . v - (S/n) . v in fp64, keyed by float(p_i);
+//   4. the floor(c/2)*G members of smallest key, equal keys lowest position
+//      first, go left, the rest right, both in their previous order (members
+//      stay in ascending token order, so position order is index order).
+//
+// Two schedules.  Levels whose nodes are larger than `cr` rows (the top of
+// the tree, few nodes) are spread over many workgroups: row chunks of cr
+// rows produce partial sums (step 1), an ordered reduction adds them, one
+// workgroup per node iterates (step 2), row chunks project (step 3) and one
+// workgroup per node splits (step 4, select.hpp).  Smaller nodes are done by
+// one workgroup each from start to end, with the projection keys and member
+// ids kept in registers.
+//
+// In step 1 the gathered rows of a 64-row tile are copied straight into LDS
+// (global_load_lds, 16 bytes per lane) in a two-slot ring, row-major with the
+// 16-byte chunks XOR-swizzled per row; both MFMA operands (x^T blocks) are
+// read with ds_read_b64_tr_b16.  Wave w holds column block w of the scatter
+// matrix in the MFMA output layout (lane: one column, 16 rows per 32-row
+// block), so C v needs only an in-lane sum and one half-wave exchange.
+#include <algorithm>
+#include <type_traits>
+
 #include "mcs_kernels.hpp"
+#include "ring.hpp"
+#include "select.hpp"
 
 namespace mcs {
 namespace {
+
+constexpr int kNodeThreads = 256;
+constexpr int kSplitThreads = 512;
+constexpr int kProjRows = 512;      // rows per workgroup of the projection kernel
+constexpr int kMaxChunkRows = 4096;  // row chunk of the many-workgroup levels; larger nodes split there
 
 struct PddpParams {
   const void* Q;
   int32_t* perm;
   int32_t* tmp;
   uint32_t* keys;
-  int Nq, G, iters, level;
+  double* part;  // [BH][nslots][pmax][D + D*D] partial (S, sum x x^T) per row chunk
+  double* red;   // [BH][nslots][D + D*D] their sums
+  double* vec;   // [BH][nslots][D + 1] direction v and (S/n) . v
+  int Nq, G, iters, level, cr, pmax;
+  int pj_pmax;  // projection chunks (of kProjRows rows) per node at this level
 };
 
-__device__ __forceinline__ int scan256(int v, int* s_wsum) {
-  const int w = wave_id();
-  const int x = wave_incl_scan(v);
-  if (lane_id() == 63) s_wsum[w] = x;
-  __syncthreads();
-  int off = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) off += (i < w) ? s_wsum[i] : 0;
-  __syncthreads();
-  return x + off;
-}
+struct Node {
+  int start, n, c;
+};
 
-__global__ void pddp_init_kernel(int32_t* perm, int Nq, size_t total) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < total) perm[i] = (int32_t)(i % (size_t)Nq);
-}
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void pddp_level_kernel(PddpParams p) {
-  constexpr int NB = D / 32;
-  constexpr int XS = 64 + 8;  // transposed bf16 staging: row = one channel, 64 query rows
-  constexpr int FS = D + 4;   // fp32 staging: row = one query row
-  constexpr int STAGE_BYTES = BF16 ? D * XS * 2 : 64 * FS * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char stage_raw[STAGE_BYTES];
-  __shared__ double sS[D], sV[D];
-  __shared__ double sRed[4];
-  __shared__ int hist[256];
-  __shared__ int s_wsum[4];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
-  __shared__ int s_tot[2];
-
-  const int bh = blockIdx.y, slot = blockIdx.x;
-  int start = 0, n = p.Nq, c = (p.Nq + p.G - 1) / p.G;
-  for (int b = p.level - 1; b >= 0; --b) {
-    if (c <= 1) return;
-    const int cL = c >> 1, nL = cL * p.G;
+// Shape of node `slot` of `level` (c == 0: the slot lies under a leaf).
+__device__ __forceinline__ Node pddp_node(int slot, int level, int Nq, int G) {
+  Node nd{0, Nq, (Nq + G - 1) / G};
+  for (int b = level - 1; b >= 0; --b) {
+    if (nd.c <= 1) return Node{0, 0, 0};
+    const int cL = nd.c >> 1, nL = cL * G;
     if ((slot >> b) & 1) {
-      start += nL;
-      n -= nL;
-      c -= cL;
+      nd.start += nL;
+      nd.n -= nL;
+      nd.c -= cL;
     } else {
-      n = nL;
-      c = cL;
+      nd.n = nL;
+      nd.c = cL;
     }
   }
-  if (c <= 1) return;
-  const int nL = (c >> 1) * p.G;
-  const size_t hbase = (size_t)bh * p.Nq;
-  int32_t* nperm = p.perm + hbase + start;
-  uint32_t* nkeys = p.keys + hbase + start;
-  int32_t* ntmp = p.tmp + hbase + start;
+  return nd;
+}
 
+template <int D>
+struct GramCfg {
+  static constexpr int NB = D / 32;
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int RPL = 64 / CH;       // rows per wave-wide copy
+  static constexpr int LPW = 64 / RPL / 4;  // wave-wide copies per wave per 64-row tile
+  static constexpr int TILE_BYTES = 64 * D * 2;
+  static constexpr int FS = D + 4;          // fp32 staging row stride
+};
+
+template <int D, bool BF16>
+struct GramLds {
+  static constexpr int SLOT0 = BF16 ? GramCfg<D>::TILE_BYTES : 64 * GramCfg<D>::FS * 4;
+  static constexpr int SLOT1 = BF16 ? GramCfg<D>::TILE_BYTES : 16;
+};
+
+// Step 1 over member rows [r0, r1) of a node (nperm: the node's members).
+// cacc (waves w < NB): sum x x^T, element (bi, i) = row 32*bi + 8*(i/4) +
+// 4*h + i%4, column 32*w + lane%32.  sS[0..D): sum x.  Ends with a barrier.
+template <int D, bool BF16>
+__device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
+                          unsigned char* slot0, unsigned char* slot1, double (&cacc)[D / 32][16], double* sS) {
+  using C = GramCfg<D>;
+  constexpr int NB = C::NB;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
-  const bool gw = w < NB;  // wave owns column block w of C
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cacc[bi][i] = 0.0;
 
-  // ---- 1. sums and raw scatter --------------------------------------------
-  double cacc[NB][16];
+  if constexpr (BF16) {
+    const __bf16* Qh = (const __bf16*)Qv + hbase * D;
+    // operand reads (transposing): lane l gets channel 32*b + l%32 of rows
+    // 4h + j (first read) and 8 + 4h + j (second read), j = 0..3, of each
+    // 16-row step; rows enter both operands in the same order
+    const int vr = 4 * h + ((l & 15) >> 2);
+    const int c0 = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+    const int ob0 = vr * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(vr));
+    const int ob1 = (8 + vr) * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(8 + vr));
+    const int lrow0 = l / C::CH, lchunk = l % C::CH;
+    const int ntiles = (r1 - r0 + 63) / 64;
+    // column sums: lane (n, h) of wave w keeps element n%16 of the ones-product,
+    // i.e. S[32w + 8((n%16)/4) + 4h + n%4]
+    double sacc = 0.0;
+    const int si = ln & 15;
+    int ids[C::LPW];
+    auto load_ids = [&](int t) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cacc[b][i] = 0.0;
-  double ssum = 0.0;
-  for (int r0 = 0; r0 < n; r0 += 64) {
-    const int rows = min(64, n - r0);
-    if constexpr (BF16) {
-      __bf16* Xt = (__bf16*)stage_raw;
-      const __bf16* Qb = (const __bf16*)p.Q;
-      for (int e = tid; e < 64 * (D / 8); e += 256) {
-        const int r = e / (D / 8), ch = e % (D / 8);
-        bf16x8 v = {};
-        if (r < rows) v = *(const bf16x8*)(Qb + (hbase + nperm[r0 + r]) * D + ch * 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) Xt[(ch * 8 + j) * XS + r] = v[j];
+      for (int j = 0; j < C::LPW; ++j) {
+        const int r = C::RPL * (w + 4 * j) + lrow0;
+        ids[j] = nperm[min(r0 + t * 64 + r, r1 - 1)];  // tail rows repeat the last row (masked below)
       }
-    } else {
-      float* Xs = (float*)stage_raw;
-      const float* Qf = (const float*)p.Q;
-      for (int e = tid; e < 64 * (D / 4); e += 256) {
+    };
+    auto issue = [&](unsigned char* slot) {
+#pragma unroll
+      for (int j = 0; j < C::LPW; ++j) {
+        const int li = w + 4 * j;
+        const int r = C::RPL * li + lrow0;
+        dma16(Qh + (size_t)ids[j] * D + ((lchunk ^ swz<D>(r)) * 8), slot + li * 1024);
+      }
+    };
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
+    // x^T operand of channel block b for 16-row step ks2, rows >= valid zeroed
+    auto operand = [&](const unsigned char* slot, int b, int ks2, int valid) {
+      const unsigned char* base = slot + 16 * (2 * D) * ks2;
+      bf16x8 op = cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
+      if (valid < 64) {
+        const __bf16 z = (__bf16)0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          op[j] = 16 * ks2 + 4 * h + j < valid ? op[j] : z;
+          op[4 + j] = 16 * ks2 + 8 + 4 * h + j < valid ? op[4 + j] : z;
+        }
+      }
+      return op;
+    };
+    // two fp32 accumulators live at a time (row blocks outer), which keeps the
+    // kernel within 256 registers per lane
+    auto compute = [&](const unsigned char* slot, int valid) {
+      if (w >= NB) return;
+      bf16x8 ow[4];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) ow[ks2] = operand(slot, w, ks2, valid);
+      f32x16 accS = {};
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) accS = mfma_32x32x16(ow[ks2], ones, accS);
+#pragma unroll
+      for (int bi = 0; bi < NB; bi += 2) {  // two independent accumulators
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks2 = 0; ks2 < 4; ++ks2) {
+          acc0 = mfma_32x32x16(operand(slot, bi, ks2, valid), ow[ks2], acc0);
+          acc1 = mfma_32x32x16(operand(slot, bi + 1, ks2, valid), ow[ks2], acc1);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          cacc[bi][i] += (double)acc0[i];
+          cacc[bi + 1][i] += (double)acc1[i];
+        }
+      }
+      float sv = accS[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) sv = (si == i) ? accS[i] : sv;
+      sacc += (double)sv;
+    };
+    if (ntiles > 0) {
+      load_ids(0);
+      issue(slot0);
+      if (ntiles > 1) load_ids(1);
+    }
+    for (int t = 0; t < ntiles; t += 2) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        issue(slot1);
+        if (t + 2 < ntiles) load_ids(t + 2);
+      }
+      compute(slot0, r1 - r0 - t * 64);
+      if (t + 1 >= ntiles) break;
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (t + 2 < ntiles) {
+        issue(slot0);
+        if (t + 3 < ntiles) load_ids(t + 3);
+      }
+      compute(slot1, r1 - r0 - (t + 1) * 64);
+    }
+    if (w < NB && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = sacc;
+    __syncthreads();
+  } else {
+    const float* Qf = (const float*)Qv + hbase * D;
+    float* Xs = (float*)slot0;
+    double ssum = 0.0;
+    for (int rr = r0; rr < r1; rr += 64) {
+      const int rows = min(64, r1 - rr);
+      for (int e = tid; e < 64 * (D / 4); e += blockDim.x) {
         const int r = e / (D / 4), ch = e % (D / 4);
         f32x4 v = {};
-        if (r < rows) v = *(const f32x4*)(Qf + (hbase + nperm[r0 + r]) * D + ch * 4);
-        *(f32x4*)(Xs + r * FS + ch * 4) = v;
+        if (r < rows) v = *(const f32x4*)(Qf + (size_t)nperm[rr + r] * D + ch * 4);
+        *(f32x4*)(Xs + r * C::FS + ch * 4) = v;
       }
-    }
-    __syncthreads();
-    if (tid < D) {
-      if constexpr (BF16) {
-        const __bf16* Xt = (const __bf16*)stage_raw;
-        for (int r = 0; r < 64; ++r) ssum += (double)(float)Xt[tid * XS + r];
-      } else {
-        const float* Xs = (const float*)stage_raw;
-        for (int r = 0; r < 64; ++r) ssum += (double)Xs[r * FS + tid];
-      }
-    }
-    if (gw) {
-      if constexpr (BF16) {
-        const __bf16* Xt = (const __bf16*)stage_raw;
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-          f32x16 a32 = {};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 A = *(const bf16x8*)(Xt + (bi * 32 + ln) * XS + ks * 16 + 8 * h);
-            const bf16x8 B = *(const bf16x8*)(Xt + (w * 32 + ln) * XS + ks * 16 + 8 * h);
-            a32 = mfma_32x32x16(A, B, a32);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) cacc[bi][i] += (double)a32[i];
-        }
-      } else {
-        const float* Xs = (const float*)stage_raw;
+      __syncthreads();
+      if (tid < D)
+        for (int r = 0; r < 64; ++r) ssum += (double)Xs[r * C::FS + tid];
+      if (w < NB) {
         for (int r = 0; r < 64; ++r) {
-          const double xc = (double)Xs[r * FS + w * 32 + ln];
+          const double xc = (double)Xs[r * C::FS + w * 32 + ln];
 #pragma unroll
           for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              cacc[bi][i] = fma((double)Xs[r * FS + bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], xc, cacc[bi][i]);
+              cacc[bi][i] = fma((double)Xs[r * C::FS + bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], xc, cacc[bi][i]);
         }
       }
+      __syncthreads();
     }
+    if (tid < D) sS[tid] = ssum;
     __syncthreads();
   }
+}
 
-  // ---- 2. centre and power-iterate -----------------------------------------
-  if (tid < D) sS[tid] = ssum;
-  __syncthreads();
+// Step 2.  cacc holds sum x x^T (layout of gram_rows), sS the column sums
+// (visible to all threads).  Leaves v in sV and returns (S/n) . v.
+// With v_k = y_k / ||y_k||, the iteration runs as y_{k+1} = C y_k / ||y_k||:
+// the norm of y_k is reduced while y_{k+1} is formed, so one barrier per step
+// suffices (y double-buffered in sY).  If C v_k = 0 the direction stays v_k.
+template <int D>
+__device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* sS, double* sV, double (*sY)[D],
+                                     double (*sRed)[4], int n, int iters) {
+  constexpr int NB = D / 32;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
+  const bool gw = w < NB;
   const double inv_n = 1.0 / (double)n;
   if (gw) {
     const double sc = sS[w * 32 + ln] * inv_n;
@@ -171,139 +261,431 @@ __global__ __launch_bounds__(256) void pddp_level_kernel(PddpParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) cacc[bi][i] -= sS[bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)] * sc;
   }
-  if (tid < D) sV[tid] = 1.0 / sqrt((double)D);
+  // y_0 = v_0 = 1/sqrt(d) (unit norm)
+  if (tid < D) sY[0][tid] = 1.0 / sqrt((double)D);
+  if (tid < 4) sRed[0][tid] = tid == 0 ? 1.0 : 0.0;
   __syncthreads();
-  for (int it = 0; it < p.iters; ++it) {
+  int cur = 0;   // buffer holding y_k
+  int last = 0;  // buffer of the last y with a nonzero norm
+  for (int it = 0; it < iters; ++it) {
+    const double nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
+    if (nrm2 == 0.0) break;  // C v = 0: keep the previous direction
+    last = cur;
+    const double inv = 1.0 / sqrt(nrm2);
     double wv = 0.0;
     if (gw) {
+      double part[NB];  // independent FMA chains, one per row block
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int bi = 0; bi < NB; ++bi) {
+        part[bi] = 0.0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) wv = fma(cacc[bi][i], sV[bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], wv);
-      wv += __shfl_xor(wv, 32, 64);
+        for (int i = 0; i < 16; ++i) part[bi] = fma(cacc[bi][i], sY[cur][bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], part[bi]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) wv += part[bi];
+      wv += partner32_f64(wv);
+      wv *= inv;
     }
     const double sq = wave_sum_f64((gw && h == 0) ? wv * wv : 0.0);
-    if (l == 0) sRed[w] = sq;
+    const int nxt = cur ^ 1;
+    if (gw && h == 0) sY[nxt][w * 32 + ln] = wv;
+    if (l == 0 && w < 4) sRed[nxt][w] = gw ? sq : 0.0;
     __syncthreads();
-    const double tot = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
-    if (tot == 0.0) break;  // degenerate node: keep the current direction
-    const double inv = 1.0 / sqrt(tot);
-    if (gw && h == 0) sV[w * 32 + ln] = wv * inv;
-    __syncthreads();
+    cur = nxt;
   }
-
-  // ---- 3. projections -------------------------------------------------------
   {
-    const double mv = wave_sum_f64(tid < D ? sS[tid] * inv_n * sV[tid] : 0.0);
-    __syncthreads();
-    if (l == 0) sRed[w] = mv;
-    __syncthreads();
+    const double nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
+    if (nrm2 != 0.0) last = cur;
   }
-  const double muv = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
-  for (int i = tid; i < n; i += 256) {
-    const size_t row = (hbase + nperm[i]) * D;
-    double dot = 0.0;
+  const double nl = (sRed[last][0] + sRed[last][1]) + (sRed[last][2] + sRed[last][3]);
+  const double inv = 1.0 / sqrt(nl);
+  if (tid < D) sV[tid] = sY[last][tid] * inv;
+  __syncthreads();
+  const double mv = wave_sum_f64(tid < D ? sS[tid] * inv_n * sV[tid] : 0.0);
+  if (l == 0 && w < 4) sRed[cur ^ 1][w] = mv;  // buffer no longer read
+  __syncthreads();
+  const double muv = (sRed[cur ^ 1][0] + sRed[cur ^ 1][1]) + (sRed[cur ^ 1][2] + sRed[cur ^ 1][3]);
+  __syncthreads();
+  return muv;
+}
+
+// Step 3: projections of whole rows by groups of D/8 lanes (8 channels per
+// lane, one coalesced row read per group); the key is the flipped order key
+// of float(x . v - muv), so that the left child (smallest projections) is the
+// selection of largest keys.
+template <int D, bool BF16>
+struct RowProjector {
+  static constexpr int LPR = D / 8;     // lanes per row
+  static constexpr int RPW = 64 / LPR;  // rows per wave step
+  double vv[8];
+  int q;
+  __device__ __forceinline__ void init(const double* sV) {
+    q = lane_id() % LPR;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vv[j] = sV[8 * q + j];
+  }
+  using Raw = typename std::conditional<BF16, bf16x8, f32x4[2]>::type;
+  struct Row {
+    Raw x;
+  };
+  __device__ __forceinline__ Row load(const void* Qv, size_t row) const {
+    Row r;
     if constexpr (BF16) {
-      const __bf16* qp = (const __bf16*)p.Q + row;
-#pragma unroll
-      for (int ch = 0; ch < D / 8; ++ch) {
-        const bf16x8 v = *(const bf16x8*)(qp + ch * 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dot = fma((double)(float)v[j], sV[ch * 8 + j], dot);
-      }
+      r.x = *(const bf16x8*)((const __bf16*)Qv + row * D + 8 * q);
     } else {
-      const float* qp = (const float*)p.Q + row;
-#pragma unroll
-      for (int ch = 0; ch < D / 4; ++ch) {
-        const f32x4 v = *(const f32x4*)(qp + ch * 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dot = fma((double)v[j], sV[ch * 4 + j], dot);
-      }
+      const float* qp = (const float*)Qv + row * D + 8 * q;
+      r.x[0] = *(const f32x4*)qp;
+      r.x[1] = *(const f32x4*)(qp + 4);
     }
-    const float pf = (float)(dot - muv) + 0.0f;  // + 0 folds -0 into +0
-    nkeys[i] = float_order_key(pf);
+    return r;
+  }
+  // Every lane of the row's group returns the key.
+  __device__ __forceinline__ uint32_t key(const Row& r, double muv) const {
+    double d = 0.0;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d = fma((double)(float)r.x[j], vv[j], d);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d = fma((double)r.x[0][j], vv[j], d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d = fma((double)r.x[1][j], vv[4 + j], d);
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o, 64);
+    const float pf = (float)(d - muv) + 0.0f;  // + 0 folds -0 into +0
+    return ~float_order_key(pf);
+  }
+};
+
+// Keys of member rows [r0, r1) (positions within the node): f(i, key) once per row.
+template <int D, bool BF16, int NT, class F>
+__device__ __forceinline__ void project_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
+                                             const double* sV, double muv, F&& f) {
+  using P = RowProjector<D, BF16>;
+  P pr;
+  pr.init(sV);
+  constexpr int U = 4;  // rows per lane group in flight
+  const int w = wave_id(), sub = lane_id() / P::LPR;
+  const int step = NT / 64 * P::RPW;
+  for (int b = r0 + w * P::RPW; b < r1; b += U * step) {
+    int id[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) id[u] = nperm[min(b + u * step + sub, r1 - 1)];
+    typename P::Row x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = pr.load(Qv, hbase + id[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b + u * step + sub;
+      const uint32_t k = pr.key(x[u], muv);
+      if (i < r1 && pr.q == 0) f(i, k);
+    }
+  }
+}
+
+struct NoKeys {
+  __device__ __forceinline__ uint32_t operator()(int) const { return 0u; }
+};
+
+struct LdsKeys {
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int j) const { return k[j]; }
+};
+
+struct GlobalKeys {
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t operator()(int j) const { return k[j]; }
+};
+
+// ---- one workgroup per node ------------------------------------------------
+template <int D, bool BF16, int VPT>
+__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void pddp_node_kernel(PddpParams p) {
+  using L = GramLds<D, BF16>;
+  using Sel = BlockSelect<kNodeThreads, VPT>;
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[L::SLOT0];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
+  __shared__ double sS[D], sV[D], sY[2][D], sRed[2][4];
+  __shared__ typename Sel::Shared sh;
+  __shared__ uint32_t s_keys[VPT * kNodeThreads];
+  const int bh = blockIdx.y;
+  const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
+  if (nd.c <= 1) return;
+  const size_t hbase = (size_t)bh * p.Nq;
+  int32_t* nperm = p.perm + hbase + nd.start;
+  double cacc[D / 32][16];
+  gram_rows<D, BF16>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, cacc, sS);
+  const double muv = centre_and_iterate<D>(cacc, sS, sV, sY, sRed, nd.n, p.iters);
+  project_rows<D, BF16, kNodeThreads>(p.Q, hbase, nperm, 0, nd.n, sV, muv, [&](int i, uint32_t k) { s_keys[i] = k; });
+  __syncthreads();
+  Sel sel;
+  sel.n = nd.n;
+  int ids[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) ids[i] = nperm[min(i * kNodeThreads + (int)threadIdx.x, nd.n - 1)];
+  sel.load(LdsKeys{s_keys});
+  const int nL = (nd.c >> 1) * p.G;
+  uint32_t T;
+  int tie_need;
+  sel.threshold(NoKeys{}, nL, sh, T, tie_need);  // its barriers also retire every read of nperm
+  sel.split(NoKeys{}, T, tie_need, sh, [&](int i, int, bool s, int pos) {
+    const int dst = s ? pos : nL + pos;
+    if (dst < nd.n) nperm[dst] = ids[i];
+  });
+}
+
+// ---- many workgroups per node ---------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void pddp_gram_kernel(PddpParams p) {
+  using L = GramLds<D, BF16>;
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[L::SLOT0];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
+  __shared__ double sS[D];
+  const int bh = blockIdx.y, slot = blockIdx.x / p.pmax, chunk = blockIdx.x % p.pmax;
+  const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
+  if (nd.c <= 1) return;
+  const int r0 = chunk * p.cr;
+  if (r0 >= nd.n) return;
+  const int r1 = min(nd.n, r0 + p.cr);
+  const size_t hbase = (size_t)bh * p.Nq;
+  double cacc[D / 32][16];
+  gram_rows<D, BF16>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, cacc, sS);
+  const int nslots = 1 << p.level;
+  double* out = p.part + (((size_t)bh * nslots + slot) * p.pmax + chunk) * (D + D * D);
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
+  if (tid < D) out[tid] = sS[tid];
+  if (w < D / 32) {
+#pragma unroll
+    for (int bi = 0; bi < D / 32; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        out[D + (size_t)(32 * bi + 8 * (i >> 2) + 4 * h + (i & 3)) * D + 32 * w + ln] = cacc[bi][i];
+  }
+}
+
+// Ordered sum of a node's partials (same order on every run).
+template <int D>
+__global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
+  constexpr int E = D + D * D;
+  constexpr int RB = (E + 255) / 256;
+  const int bh = blockIdx.y, slot = blockIdx.x / RB;
+  const int e = (blockIdx.x % RB) * 256 + threadIdx.x;
+  const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
+  if (nd.c <= 1 || e >= E) return;
+  const int parts = (nd.n + p.cr - 1) / p.cr;
+  const size_t node = (size_t)bh * (1 << p.level) + slot;
+  const double* src = p.part + node * p.pmax * E + e;
+  double s = 0.0;
+  for (int q = 0; q < parts; ++q) s += src[(size_t)q * E];
+  p.red[node * E + e] = s;
+}
+
+template <int D>
+__global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) {
+  constexpr int E = D + D * D;
+  __shared__ double sS[D], sV[D], sY[2][D], sRed[2][4];
+  const int bh = blockIdx.y, slot = blockIdx.x;
+  const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
+  if (nd.c <= 1) return;
+  const size_t node = (size_t)bh * (1 << p.level) + slot;
+  const double* red = p.red + node * E;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
+  double cacc[D / 32][16];
+  if (tid < D) sS[tid] = red[tid];
+  if (w < D / 32) {
+#pragma unroll
+    for (int bi = 0; bi < D / 32; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        cacc[bi][i] = red[D + (size_t)(32 * bi + 8 * (i >> 2) + 4 * h + (i & 3)) * D + 32 * w + ln];
   }
   __syncthreads();
-
-  // ---- 4. rank select and stable partition ---------------------------------
-  uint32_t prefix = 0, pmask = 0;
-  int krem = nL;  // rank (from the bottom) still to locate among keys matching prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t u = nkeys[i];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
-    }
-    __syncthreads();
-    const int cnt = hist[tid];
-    const int cum = scan256(cnt, s_wsum);
-    if (cum >= krem && cum - cnt < krem) {
-      s_prefix = prefix | ((uint32_t)tid << shift);
-      s_krem = krem - (cum - cnt);
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
-    pmask |= 0xFFu << shift;
-  }
-  const uint32_t T = prefix;
-  int base_left = 0, base_tie = 0;
-  for (int s0 = 0; s0 < n; s0 += 256) {
-    const int i = s0 + tid;
-    const bool valid = i < n;
-    const uint32_t u = valid ? nkeys[i] : 0xFFFFFFFFu;
-    const int lt = (valid && u < T) ? 1 : 0;
-    const int eq = (valid && u == T) ? 1 : 0;
-    const int tie_incl = scan256(eq, s_wsum);
-    const int left = (lt || (eq && base_tie + tie_incl - eq < krem)) ? 1 : 0;
-    const int left_incl = scan256(left, s_wsum);
-    if (valid) {
-      const int lpos = base_left + left_incl - left;
-      ntmp[left ? lpos : nL + (i - lpos)] = nperm[i];
-    }
-    if (tid == 255) {
-      s_tot[0] = tie_incl;
-      s_tot[1] = left_incl;
-    }
-    __syncthreads();
-    base_tie += s_tot[0];
-    base_left += s_tot[1];
-    __syncthreads();
-  }
-  for (int i = tid; i < n; i += 256) nperm[i] = ntmp[i];
+  const double muv = centre_and_iterate<D>(cacc, sS, sV, sY, sRed, nd.n, p.iters);
+  double* out = p.vec + node * (D + 1);
+  if (tid < D) out[tid] = sV[tid];
+  if (tid == 0) out[D] = muv;
 }
 
 template <int D, bool BF16>
-void launch_levels(const Shape& s, const void* Q, int32_t* perm, int32_t* tmp, uint32_t* keys, hipStream_t st) {
-  int levels = 0;
-  while ((1 << levels) < s.c) ++levels;
-  PddpParams p{Q, perm, tmp, keys, s.Nq, s.G, s.iters, 0};
-  for (int lv = 0; lv < levels; ++lv) {
+__global__ __launch_bounds__(256) void pddp_project_kernel(PddpParams p) {
+  __shared__ double sV[D];
+  __shared__ double s_muv;
+  const int bh = blockIdx.y, slot = blockIdx.x / p.pj_pmax, chunk = blockIdx.x % p.pj_pmax;
+  const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
+  if (nd.c <= 1) return;
+  const int r0 = chunk * kProjRows;
+  if (r0 >= nd.n) return;
+  const int r1 = min(nd.n, r0 + kProjRows);
+  const size_t node = (size_t)bh * (1 << p.level) + slot;
+  const double* vec = p.vec + node * (D + 1);
+  if ((int)threadIdx.x < D) sV[threadIdx.x] = vec[threadIdx.x];
+  if (threadIdx.x == 0) s_muv = vec[D];
+  __syncthreads();
+  const double muv = s_muv;
+  const size_t hbase = (size_t)bh * p.Nq;
+  uint32_t* nkeys = p.keys + hbase + nd.start;
+  project_rows<D, BF16, 256>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, sV, muv,
+                             [&](int i, uint32_t k) { nkeys[i] = k; });
+}
+
+template <int VPT>
+__global__ __launch_bounds__(kSplitThreads) void pddp_split_kernel(PddpParams p) {
+  using Sel = BlockSelect<kSplitThreads, VPT>;
+  __shared__ typename Sel::Shared sh;
+  const int bh = blockIdx.y;
+  const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
+  if (nd.c <= 1) return;
+  const size_t off = (size_t)bh * p.Nq + nd.start;
+  int32_t* nperm = p.perm + off;
+  int32_t* ntmp = p.tmp + off;
+  const GlobalKeys keys{p.keys + off};
+  const int nL = (nd.c >> 1) * p.G;
+  Sel sel;
+  sel.n = nd.n;
+  sel.load(keys);
+  uint32_t T;
+  int tie_need;
+  sel.threshold(keys, nL, sh, T, tie_need);
+  // new position -> old position, then a batched gather through the key
+  // array (no longer needed) and a copy back
+  sel.split(keys, T, tie_need, sh, [&](int, int j, bool s, int pos) {
+    const int dst = s ? pos : nL + pos;
+    if (dst < nd.n) ntmp[dst] = j;
+  });
+  __syncthreads();
+  int32_t* staged = (int32_t*)(p.keys + off);
+  constexpr int U = 8;
+  for (int i0 = 0; i0 < nd.n; i0 += U * kSplitThreads) {
+    int src[U], val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) src[u] = ntmp[min(i0 + u * kSplitThreads + (int)threadIdx.x, nd.n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) val[u] = nperm[min(max(src[u], 0), nd.n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kSplitThreads + (int)threadIdx.x;
+      if (i < nd.n) staged[i] = val[u];
+    }
+  }
+  __syncthreads();
+  for (int i0 = 0; i0 < nd.n; i0 += U * kSplitThreads) {
+    int val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) val[u] = staged[min(i0 + u * kSplitThreads + (int)threadIdx.x, nd.n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kSplitThreads + (int)threadIdx.x;
+      if (i < nd.n) nperm[i] = val[u];
+    }
+  }
+}
+
+__global__ void pddp_init_kernel(int32_t* perm, int Nq, size_t total) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < total) perm[i] = (int32_t)(i % (size_t)Nq);
+}
+
+// Host-side plan: the tree's shape depends only on Nq and G.
+struct Plan {
+  int levels, cr;
+  size_t part, red, vec;  // doubles
+};
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+long long level_max_rows(const Shape& s, int level) {
+  const long long cmax = ((long long)s.c + (1LL << level) - 1) >> level;
+  const long long n = cmax * s.G;
+  return n < s.Nq ? n : s.Nq;
+}
+
+Plan make_plan(const Shape& s) {
+  Plan pl{0, 0, 0, 0, 0};
+  while ((1 << pl.levels) < s.c) ++pl.levels;
+  long long cr = ((long long)s.BH * s.Nq + 511) / 512;
+  cr = (cr + 63) / 64 * 64;
+  pl.cr = (int)(cr < 2048 ? 2048 : (cr > kMaxChunkRows ? kMaxChunkRows : cr));
+  const size_t E = (size_t)s.d + (size_t)s.d * s.d;
+  for (int lv = 0; lv < pl.levels; ++lv) {
+    const long long maxn = level_max_rows(s, lv);
+    if (maxn <= pl.cr) break;
+    const size_t nodes = (size_t)s.BH << lv;
+    const size_t pmax = (size_t)((maxn + pl.cr - 1) / pl.cr);
+    pl.part = std::max(pl.part, nodes * pmax * E);
+    pl.red = std::max(pl.red, nodes * E);
+    pl.vec = std::max(pl.vec, nodes * ((size_t)s.d + 1));
+  }
+  return pl;
+}
+
+template <int D, bool BF16>
+void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st) {
+  constexpr int RB = (D + D * D + 255) / 256;
+  for (int lv = 0; lv < pl.levels; ++lv) {
     p.level = lv;
-    hipLaunchKernelGGL((pddp_level_kernel<D, BF16>), dim3(1u << lv, s.BH), dim3(256), 0, st, p);
+    const int nslots = 1 << lv;
+    const long long maxn = level_max_rows(s, lv);
+    if (maxn > pl.cr) {
+      p.pmax = (int)((maxn + pl.cr - 1) / pl.cr);
+      const dim3 chunks(nslots * p.pmax, s.BH);
+      hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
+      hipLaunchKernelGGL((pddp_reduce_kernel<D>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((pddp_power_kernel<D>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
+      p.pj_pmax = (int)((maxn + kProjRows - 1) / kProjRows);
+      hipLaunchKernelGGL((pddp_project_kernel<D, BF16>), dim3(nslots * p.pj_pmax, s.BH), dim3(256), 0, st, p);
+      if (maxn <= 64LL * kSplitThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<64>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+      else
+        hipLaunchKernelGGL((pddp_split_kernel<0>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+    } else {
+      const dim3 grid(nslots, s.BH);
+      static_assert(kMaxChunkRows <= 16 * kNodeThreads, "node kernel register cache");
+      if (maxn <= 2 * kNodeThreads)
+        hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 2>), grid, dim3(kNodeThreads), 0, st, p);
+      else if (maxn <= 8 * kNodeThreads)
+        hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 8>), grid, dim3(kNodeThreads), 0, st, p);
+      else
+        hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 16>), grid, dim3(kNodeThreads), 0, st, p);
+    }
   }
 }
 
 }  // namespace
 
 size_t pddp_workspace_bytes(const Shape& s) {
+  const Plan pl = make_plan(s);
   const size_t n = (size_t)s.BH * s.Nq;
-  return ((n * 4 + 255) / 256) * 256 * 2;
+  return 2 * round256(n * 4) + round256(pl.part * 8) + round256(pl.red * 8) + round256(pl.vec * 8);
 }
 
 hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, void* ws, hipStream_t st) {
+  const Plan pl = make_plan(s);
   const size_t n = (size_t)s.BH * s.Nq;
-  int32_t* tmp = (int32_t*)ws;
-  uint32_t* keys = (uint32_t*)((char*)ws + ((n * 4 + 255) / 256) * 256);
+  char* w = (char*)ws;
+  PddpParams p{};
+  p.Q = Q;
+  p.perm = perm;
+  p.tmp = (int32_t*)w;
+  w += round256(n * 4);
+  p.keys = (uint32_t*)w;
+  w += round256(n * 4);
+  p.part = (double*)w;
+  w += round256(pl.part * 8);
+  p.red = (double*)w;
+  w += round256(pl.red * 8);
+  p.vec = (double*)w;
+  p.Nq = s.Nq;
+  p.G = s.G;
+  p.iters = s.iters;
+  p.cr = pl.cr;
+  p.pmax = 1;
   hipLaunchKernelGGL(pddp_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, perm, s.Nq, n);
   if (bf16) {
-    if (s.d == 128) launch_levels<128, true>(s, Q, perm, tmp, keys, st);
-    else launch_levels<64, true>(s, Q, perm, tmp, keys, st);
+    if (s.d == 128) launch_levels<128, true>(s, pl, p, st);
+    else launch_levels<64, true>(s, pl, p, st);
   } else {
-    if (s.d == 128) launch_levels<128, false>(s, Q, perm, tmp, keys, st);
-    else launch_levels<64, false>(s, Q, perm, tmp, keys, st);
+    if (s.d == 128) launch_levels<128, false>(s, pl, p, st);
+    else launch_levels<64, false>(s, pl, p, st);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,218 @@
+// Exact block-wide selection of the `need` largest 32-bit keys of an array,
+// equal keys taken lowest index first, followed by an order-preserving split
+// of the array into the selected and the remaining elements.
+//
+// Used for the per-group token-level top-k (MC-Sparse review,
+// blog.secrett2633.cloud, section 3: each query group keeps the KV tokens of
+// largest exact attention mass) and for the rank split of every PDDP node
+// (the floor(c/2)*G members of smallest projection go left; the caller flips
+// the projection keys so that "smallest" becomes "largest").
+//
+// Element j of the array belongs to thread j % NT ("stripe" j / NT).  With
+// VPT > 0 the caller caches the keys of its VPT stripes in registers (the
+// array must then hold at most VPT * NT elements); with VPT == 0 keys are
+// re-read through a functor on every pass.  Positions j >= n of the last
+// stripe read as key 0: they sit above every real index, so they are never
+// selected ahead of a real key (at most n are selected) and every stripe can
+// be processed without lane masks; only the final emit skips them.
+//
+// Threshold: three MSB-first radix passes (12, 12 and 8 bits) over the
+// elements whose key matches the digits found so far; histograms in LDS.
+// The result is the need-th largest key T and how many keys equal to T are
+// selected.
+//
+// Split: per (stripe, wave) the counts of keys > T and == T come from two
+// ballots; one block scan over these counts gives every wave its offsets, so
+// each element knows its rank among the selected (or the remaining) elements
+// in index order without further synchronisation.  Stripes are handled in
+// blocks of 64 (three barriers per block).
+#pragma once
+
+#include "mcs_device.hpp"
+
+namespace mcs {
+
+// Exclusive block scan over NT threads; `total` receives the block sum.
+// Two barriers; s_w holds NT/64 ints.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
+  constexpr int NW = NT / 64;
+  const int w = wave_id();
+  const int x = wave_incl_scan(v);
+  if (lane_id() == 63) s_w[w] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int s = s_w[i];
+    off += (i < w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return x - v + off;
+}
+
+template <int NT, int VPT>
+struct BlockSelect {
+  static_assert(NT % 64 == 0 && NT >= 256 && NT <= 1024, "block size");
+  static constexpr int NW = NT / 64;
+  static constexpr int NBIN = 4096;
+  static constexpr int BPT = NBIN / NT;  // histogram bins owned by one thread in the rank search
+  static constexpr int VB = 64;         // stripes per split block (one per lane; VB * NW <= NT)
+  static_assert(VPT >= 0 && VPT <= VB, "register cache");
+
+  struct Shared {
+    int hist[NBIN];
+    int cnt_gt[NT];
+    int cnt_eq[NT];
+    int wsum[NW];
+    uint32_t prefix;
+    int krem;
+  };
+
+  uint32_t v[VPT > 0 ? VPT : 1];  // cached keys of stripes 0..VPT-1 (VPT > 0)
+  int n;                          // array length
+
+  // Key of position j in register mode: a clamped (unconditional) read.
+  template <class Keys>
+  __device__ __forceinline__ void load(const Keys& keys) {
+    if constexpr (VPT > 0) {
+      // an opaque copy of the thread index keeps the compiler from holding
+      // these positions (and their range tests) live until the split
+      int t = threadIdx.x;
+      asm volatile("" : "+v"(t));
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int j = i * NT + t;
+        const uint32_t u = keys(min(j, n - 1));
+        v[i] = j < n ? u : 0u;
+      }
+    }
+  }
+
+  // f(stripe, j, key) for the stripes [s0, s1) of this thread (uniform trip
+  // count; in register mode always all VPT stripes, s0 = 0 and s1 = VPT).
+  template <class Keys, class F>
+  __device__ __forceinline__ void stripes(int s0, int s1, const Keys& keys, F&& f) const {
+    const int t = threadIdx.x;
+    if constexpr (VPT > 0) {
+      // all VPT stripes, also those past the end (keys 0, see above): no
+      // per-stripe conditions to keep live
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) f(i, i * NT + t, v[i]);
+    } else {
+      for (int s = s0; s < s1; ++s) {
+        const int j = s * NT + t;
+        const uint32_t u = keys(min(j, n - 1));
+        f(s, j, j < n ? u : 0u);
+      }
+    }
+  }
+
+  // T = need-th largest key (1 <= need <= n); tie_need = how many keys equal
+  // to T belong to the selection.
+  template <class Keys>
+  __device__ void threshold(const Keys& keys, int need, Shared& sh, uint32_t& T, int& tie_need) const {
+    const int t = threadIdx.x;
+    const int top = NBIN - 1 - t * BPT;  // this thread's bins: top, top-1, ..., top-BPT+1
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) sh.hist[top - b] = 0;
+    __syncthreads();
+    const int nstripes = VPT > 0 ? VPT : (n + NT - 1) / NT;
+    uint32_t prefix = 0, pmask = 0;
+    int krem = need;  // rank, from the top, still to locate among keys matching prefix
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+      const uint32_t dmask = pass == 2 ? 0xFFu : 0xFFFu;
+      stripes(0, nstripes, keys, [&](int, int, uint32_t u) {
+        if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1);
+      });
+      __syncthreads();
+      int cnt[BPT], local = 0;
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) {
+        cnt[b] = sh.hist[top - b];
+        local += cnt[b];
+      }
+      int total;
+      const int above = block_excl_scan<NT>(local, sh.wsum, total);  // matching keys in higher bins
+      if (above < krem && above + local >= krem) {
+        int c = above;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+          if (c + cnt[b] >= krem) {
+            sh.prefix = prefix | ((uint32_t)(top - b) << shift);
+            sh.krem = krem - c;
+            break;
+          }
+          c += cnt[b];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) sh.hist[top - b] = 0;
+      __syncthreads();
+      prefix = sh.prefix;
+      krem = sh.krem;
+      pmask |= dmask << shift;
+    }
+    T = prefix;
+    tie_need = krem;
+  }
+
+  // emit(stripe, j, selected, pos) for every element j < n: pos is the rank
+  // of j among the selected elements, or among the remaining ones, in index
+  // order.
+  template <class Keys, class Emit>
+  __device__ void split(const Keys& keys, uint32_t T, int tie_need, Shared& sh, Emit&& emit) const {
+    const int w = wave_id(), l = lane_id();
+    const uint64_t below = (1ull << l) - 1ull;  // lanes with a lower index
+    const int nstripes = VPT > 0 ? VPT : (n + NT - 1) / NT;
+    int base_eq = 0, base_sel = 0;
+    for (int s0 = 0; s0 < nstripes; s0 += VB) {
+      const int s1 = min(nstripes, s0 + VB);
+      // lane i of each wave collects the counts of stripe s0 + i (VB == 64 lanes)
+      int my_gt = 0, my_eq = 0;
+      stripes(s0, s1, keys, [&](int s, int, uint32_t u) {
+        const int gtc = __popcll(__ballot(u > T)), eqc = __popcll(__ballot(u == T));
+        my_gt = (l == s - s0) ? gtc : my_gt;
+        my_eq = (l == s - s0) ? eqc : my_eq;
+      });
+      if (l < s1 - s0) {
+        sh.cnt_gt[l * NW + w] = my_gt;
+        sh.cnt_eq[l * NW + w] = my_eq;
+      }
+      __syncthreads();
+      const int e = threadIdx.x;  // entry (stripe s0 + e / NW, wave e % NW), in index order
+      const bool ein = e < (s1 - s0) * NW;
+      const int eqc = ein ? sh.cnt_eq[e] : 0, gtc = ein ? sh.cnt_gt[e] : 0;
+      int eq_tot, sel_tot;
+      const int eq_off = base_eq + block_excl_scan<NT>(eqc, sh.wsum, eq_tot);
+      const int selc = gtc + min(max(tie_need - eq_off, 0), eqc);
+      const int sel_off = base_sel + block_excl_scan<NT>(selc, sh.wsum, sel_tot);
+      if (ein) {
+        sh.cnt_eq[e] = eq_off;
+        sh.cnt_gt[e] = sel_off;
+      }
+      __syncthreads();
+      const int my_eo = l < s1 - s0 ? sh.cnt_eq[l * NW + w] : 0;
+      const int my_so = l < s1 - s0 ? sh.cnt_gt[l * NW + w] : 0;
+      stripes(s0, s1, keys, [&](int s, int j, uint32_t u) {
+        const bool g = u > T, q = u == T;
+        const uint64_t eqm = __ballot(q);
+        const int eo = __builtin_amdgcn_readlane(my_eo, s - s0);  // ties before this stripe's wave slice
+        const int so = __builtin_amdgcn_readlane(my_so, s - s0);  // selections before it
+        const bool sel = g || (q && eo + __popcll(eqm & below) < tie_need);
+        const uint64_t selm = __ballot(sel);
+        const int before = so + __popcll(selm & below);  // selected elements with a lower index
+        if (j < n) emit(s, j, sel, sel ? before : j - before);
+      });
+      base_eq += eq_tot;
+      base_sel += sel_tot;
+      if (s1 < nstripes) __syncthreads();
+    }
+  }
+};
+
+}  // namespace mcs
