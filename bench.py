@@ -42,12 +42,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for profiler counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("DB", "OUT_MD", "CMD"),
+                    help="write a markdown kernel table from a rocprofv3 kernel-trace database and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
+                    help="derive per-launch HBM traffic from FETCH_SIZE/WRITE_SIZE counter CSVs of --config, "
+                         "update profiles/traffic.json and exit")
+    ap.add_argument("--title", default="", help="title for --summarize-trace")
+    ap.add_argument("--note", default="", help="paragraph for --summarize-trace")
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+# Kernels whose HBM traffic is reported, and the sources that define them:
+# a stored counter reading is used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "sparse_ring_kernel": ("sparse_bf16.hip", "ring.hpp", "mcs_device.hpp"),
+    "dense_bf16_kernel": ("attn_bf16.hip", "mcs_device.hpp"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "mcs_device.hpp"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sparse_attention_video_pddp_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -62,9 +77,101 @@ def load_traffic(kernel: str, config: str):
     except (OSError, ValueError):
         return None
     e = t.get(kernel, {}).get(config)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    name = name.replace("void ", "").replace("mcs::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name)
+
+
+def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
+    """Markdown table of per-kernel durations from a rocprofv3 kernel-trace
+    database (via rocpd2summary)."""
+    import csv
+    import subprocess
+    import tempfile
+    tmp = tempfile.mkdtemp()
+    subprocess.run(["rocpd2summary", "-i", os.path.abspath(db), "-f", "csv", "-d", tmp], check=True,
+                   capture_output=True, cwd=tmp)
+    rows = list(csv.DictReader(open(os.path.join(tmp, "kernels_summary.csv"))))
+    with open(out, "w") as f:
+        f.write(f"# {title}\n\nCommand (repository root, one MI355X; `cd /tmp && export TMPDIR=/tmp` for the "
+                f"profiler's scratch):\n\n```\n{cmd}\n```\n\n")
+        if note:
+            f.write(note + "\n\n")
+        f.write("| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | % time |\n"
+                "|---|---:|---:|---:|---:|---:|---:|\n")
+        for r in rows:
+            name = r["Name"].replace("void ", "").replace("mcs::(anonymous namespace)::", "")
+            name = name.split("(mcs::")[0]
+            f.write(f"| `{name}` | {r['Calls']} | {float(r['Average (Nsec)']) / 1e3:.1f} | "
+                    f"{float(r['Min (Nsec)']) / 1e3:.1f} | {float(r['Max (Nsec)']) / 1e3:.1f} | "
+                    f"{float(r['Duration (Nsec)']) / 1e6:.2f} | {float(r['Percent (Inc)']):.1f} |\n")
+    print(open(out).read())
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: str, cmd_write: str) -> None:
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for the 1 GiB
+    device copy of the same run.  Reuse-kernel launches that directly follow
+    a top-k launch are anchor epilogues (they update R instead of writing O)
+    and are left out.  Writes profiles/traffic.json and a markdown summary."""
+    import csv
+    per = {}
+    for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        vals, prev = {}, ""
+        for r in rows:
+            if r["Counter_Name"] != tag:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            if not (k.startswith("sparse_ring_kernel") and prev.startswith("topk_kernel")):
+                vals.setdefault(k, []).append(float(r["Counter_Value"]))
+            prev = k
+        per[tag] = vals
+    copy = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no device copy in the counter runs (run bench.py with --copy-calibration)")
+    gib_kib = float(1 << 20)
+    f_fac = gib_kib / statistics.fmean(per["FETCH_SIZE"][copy[0]])
+    w_fac = gib_kib / statistics.fmean(per["WRITE_SIZE"][copy[0]])
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    lines = [f"# HBM traffic per launch, {config}\n",
+             "Two counter runs of the same command (repository root, one MI355X):\n",
+             f"```\n{cmd_fetch}\n{cmd_write}\n```\n",
+             f"Calibration: the 1 GiB device copy in the same runs reads FETCH_SIZE = "
+             f"{statistics.fmean(per['FETCH_SIZE'][copy[0]]):.0f} KiB and WRITE_SIZE = "
+             f"{statistics.fmean(per['WRITE_SIZE'][copy[0]]):.0f} KiB, so fetch counts are scaled by "
+             f"{f_fac:.3f} and write counts by {w_fac:.3f}.\n",
+             "| kernel | launches | fetch (MB/launch) | write (MB/launch) | total (MB/launch) |",
+             "|---|---:|---:|---:|---:|"]
+    for k in sorted(per["FETCH_SIZE"]):
+        if k not in per["WRITE_SIZE"] or "copyBuffer" in k:
+            continue
+        fb = statistics.fmean(per["FETCH_SIZE"][k]) * 1024 * f_fac
+        wb = statistics.fmean(per["WRITE_SIZE"][k]) * 1024 * w_fac
+        lines.append(f"| `{k}` | {len(per['FETCH_SIZE'][k])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                     f"{(fb + wb) / 1e6:.1f} |")
+        base = k.split("<")[0]
+        if base in KERNEL_SOURCES:
+            table.setdefault(base, {})[config] = {
+                "bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+                "launches": len(per["FETCH_SIZE"][k]), "source_hash": kernel_source_hash(base)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    out = os.path.join(ROOT, "profiles", f"traffic_{config}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(open(out).read())
 
 
 def reuse_bytes_per_launch(w) -> float:
@@ -126,6 +233,13 @@ def cpu_baseline(w, host0, host1, nheads: int):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        db, out, cmd = args.summarize_trace
+        summarize_trace(db, out, args.title or f"Kernel trace, {args.config}", cmd, args.note)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters[:2], args.config, *args.summarize_counters[2:])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every box here has one MI355X and the method's "
               "kernels run on one GPU's share; --gpus must be 1.", file=sys.stderr)
@@ -211,7 +325,7 @@ def main():
     d_mean = statistics.fmean(dense_ms)
     value = f_dense / (r_mean * 1e-3) / 1e12
     rbytes = reuse_bytes_per_launch(w)
-    traffic = load_traffic("sparse_bf16_kernel", w.name)
+    traffic = load_traffic("sparse_ring_kernel", w.name)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -246,7 +360,7 @@ def main():
         "group_ms": round(statistics.fmean(group_ms), 4),
         "anchor_ms": round(statistics.fmean(anchor_ms), 4),
         "period_effective_tflops_dense_equiv": round(A * f_dense / (wall / args.steps) / 1e12, 2),
-        "roofline": {"kernel": "sparse_bf16_kernel (mcs_sparse_attn, reuse step)", "bound": "hbm",
+        "roofline": {"kernel": "sparse_ring_kernel (mcs_sparse_attn, reuse step)", "bound": "hbm",
                      "achieved": round(rbytes / (r_mean * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(rbytes / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
