@@ -47,6 +47,18 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
+// Buffer resource over [base, base + bytes) for raw (stride 0) buffer loads:
+// a lane whose offset falls outside reads zeros.  bytes < 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Direct-to-LDS copy of 16 bytes per lane at byte offset voff of a buffer
+// (wave-uniform LDS base, lane i writes base + 16*i).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
+}
+
 template <int D>
 struct FlashCore {
   static constexpr int NB = D / 32;   // 32-channel output blocks
@@ -75,19 +87,12 @@ struct FlashCore {
     l_run = 0.f;
   }
 
-  // NKB consecutive 32-key blocks of a tile, processed jointly (one softmax
-  // update for all of them).  Ks, Vs: the first K and V rows in LDS; blocks
-  // are BLK bytes apart.  lim: keys of these blocks visible to this lane's
-  // query (any integer).
-  //
-  // LDS addresses: the K operand of k-step ks (row n, chunk (2ks+h) ^ swz(n))
-  // is Ks + (kbase ^ 32*ks); the V^T operand of channel block b (rows
-  // 16*ks2 + 8*hi + vr, chunk (4b + c0) ^ swz(row)) is
-  // Vs + (vbase_hi ^ 64*b) + 16*ks2 rows.  One XOR per read, constant offsets.
+  // Scores S^T of NKB consecutive 32-key blocks (K rows at Ks, blocks BLK
+  // bytes apart).  Element i of block kb holds key 32*kb + 8*(i/4) + 4*h + i%4.
+  // The K operand of k-step ks (row n, chunk (2ks+h) ^ swz(n)) is
+  // Ks + (kbase ^ 32*ks): one XOR per read, constant offsets.
   template <int NKB, int BLK>
-  __device__ __forceinline__ void blocks(const unsigned char* Ks, const unsigned char* Vs, int lim, float c) {
-    const int h = lane_id() >> 5;
-    f32x16 s[NKB];
+  __device__ __forceinline__ void scores(const unsigned char* Ks, f32x16 (&s)[NKB]) const {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16{};
@@ -97,6 +102,16 @@ struct FlashCore {
         s[kb] = mfma_32x32x16(a, qb[ks], s[kb]);
       }
     }
+  }
+
+  // Online softmax of the scores s (one update for all NKB blocks) and the
+  // O^T += V^T P^T product (V rows at Vs, blocks BLK bytes apart).  lim: keys
+  // of these blocks visible to this lane's query (any integer).  The V^T
+  // operand of channel block b (rows 16*ks2 + 8*hi + vr, chunk (4b + c0) ^
+  // swz(row)) is Vs + (vbase_hi ^ 64*b) + 16*ks2 rows.
+  template <int NKB, int BLK>
+  __device__ __forceinline__ void softmax_pv(f32x16 (&s)[NKB], const unsigned char* Vs, int lim, float c) {
+    const int h = lane_id() >> 5;
     // element i of block kb holds key 32*kb + 8*(i/4) + 4*h + i%4; mask keys >= lim
     const int lh = lim - 4 * h;
     if (lh < 32 * NKB - 4) {
@@ -116,6 +131,71 @@ struct FlashCore {
     const float m_ref = (m_new == -kInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_ref);
     m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+    }
+    // per 32-key block: probabilities, then O^T += V^T P^T.  A operand slot j
+    // of lane (d = l%32, half h) is key 16*ks2 + 8*(j/4) + 4*h + j%4 (the key
+    // of slot j of this lane's P^T)
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(fmaf(s[kb][i], c, -m_ref));
+        ls += pv;
+        pb[i >> 3][i & 7] = (__bf16)pv;
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int a0 = vbase0 ^ (64 * b), a1 = vbase1 ^ (64 * b);
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          const bf16x4 lo = lds_read_tr(Vs + kb * BLK + a0 + 16 * (2 * D) * ks2);
+          const bf16x4 hi = lds_read_tr(Vs + kb * BLK + a1 + 16 * (2 * D) * ks2);
+          acc[b] = mfma_32x32x16(cat(lo, hi), pb[ks2], acc[b]);
+        }
+      }
+    }
+    l_run = fmaf(l_run, alpha, ls);
+  }
+
+  // One pipelined step: softmax and O^T += V^T P^T of the tile whose scores
+  // are in s (V rows at Vs, lim visible keys), with the scores of the next
+  // tile (K rows at Kn) formed into sn in between.  The two rare branches
+  // (masking, rescaling O) come first, so the next tile's MFMAs, this tile's
+  // exponentials and its PV MFMAs share one basic block and can be
+  // interleaved.  Kn may be any tile of LDS when there is no next tile (sn is
+  // then unused).
+  template <int NKB, int BLK>
+  __device__ __forceinline__ void step(f32x16 (&s)[NKB], const unsigned char* Vs, int lim, float c,
+                                       const unsigned char* Kn, f32x16 (&sn)[NKB]) {
+    const int h = lane_id() >> 5;
+    const int lh = lim - 4 * h;
+    if (lh < 32 * NKB - 4) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kb + 8 * (i >> 2) + (i & 3) >= lh) s[kb][i] = -kInf;
+    }
+    float mx = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, partner32(mx)) * c;
+    const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
+    const float m_ref = (m_new == -kInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+    }
+    scores<NKB, BLK>(Kn, sn);
     float ls = 0.f;
     bf16x8 pb[NKB][2];
 #pragma unroll
@@ -127,12 +207,6 @@ struct FlashCore {
         pb[kb][i >> 3][i & 7] = (__bf16)pv;
       }
     l_run = fmaf(l_run, alpha, ls);
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] *= alpha;
-    }
-    // O^T += V^T P^T; A operand slot j of lane (d = l%32, half h) is key
-    // 16*ks2 + 8*(j/4) + 4*h + j%4 (the key of slot j of this lane's P^T)
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int a0 = vbase0 ^ (64 * b), a1 = vbase1 ^ (64 * b);
@@ -145,6 +219,14 @@ struct FlashCore {
           acc[b] = mfma_32x32x16(cat(lo, hi), pb[kb][ks2], acc[b]);
         }
     }
+  }
+
+  // Both steps on one tile.
+  template <int NKB, int BLK>
+  __device__ __forceinline__ void blocks(const unsigned char* Ks, const unsigned char* Vs, int lim, float c) {
+    f32x16 s[NKB];
+    scores<NKB, BLK>(Ks, s);
+    softmax_pv<NKB, BLK>(s, Vs, lim, c);
   }
 
   // 1 / row sum (0 for a row with no visible key) and the natural-log lse.

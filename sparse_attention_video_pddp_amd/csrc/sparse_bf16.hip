@@ -8,11 +8,14 @@
 //
 // One workgroup owns one (head, group): G/32 waves, 32 query columns each.
 // The group's selected K/V rows are gathered in tiles of 32 keys by
-// direct-to-LDS loads into a two-slot ring (ring.hpp): tile t+1 is in flight
-// while tile t is consumed, with one barrier per tile.  The two slots are
-// distinct LDS objects and the loop is unrolled by two, so the compiler can
-// tell the slot being read from the slot being filled and adds no wait for
-// the in-flight tile.
+// direct-to-LDS loads.  K and V have separate two-slot rings and each wave
+// runs a software pipeline: in iteration t the scores of tile t+1 (MFMA) are
+// formed next to the softmax of tile t (VALU), then O^T += V^T P^T for tile
+// t.  At the start of iteration t, after one barrier, K(t+2) goes into the
+// slot K(t) left and V(t+1) into the slot V(t-1) left; each copy is issued a
+// full iteration before it is read.  The slots are distinct LDS objects and
+// the loop is unrolled by two, so the compiler can tell the slots being read
+// from the slots being filled and adds no wait for the copies in flight.
 #include "mcs_kernels.hpp"
 #include "ring.hpp"
 
@@ -29,7 +32,6 @@ struct SparseCfg {
   static constexpr int LOADS_PER_TENSOR = TK / ROWS_PER_LOAD;
   static constexpr int LOADS_PER_WAVE = LOADS_PER_TENSOR / NW;  // per tensor
   static constexpr int TENSOR_BYTES = TK * D * 2;
-  static constexpr int SLOT_BYTES = 2 * TENSOR_BYTES;
   static_assert(LOADS_PER_WAVE >= 1 && LOADS_PER_TENSOR % NW == 0, "load split");
 };
 
@@ -48,8 +50,10 @@ template <int D, int G>
 __global__ __launch_bounds__(2 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_ring_kernel(Params p) {
   using C = SparseCfg<D, G>;
-  __shared__ __attribute__((aligned(1024))) unsigned char slot0[C::SLOT_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot1[C::SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TENSOR_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TENSOR_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TENSOR_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TENSOR_BYTES];
   extern __shared__ __attribute__((aligned(16))) int s_idx[];
   __shared__ int s_kmax[C::NW];
 
@@ -93,39 +97,51 @@ void sparse_ring_kernel(Params p) {
   int kmax = 0;
 #pragma unroll
   for (int i = 0; i < C::NW; ++i) kmax = max(kmax, s_kmax[i]);
-  const int ntiles = (kmax + C::TK - 1) / C::TK;
+  // rounded up to even: the loop below handles tiles in pairs with a single
+  // exit (a mid-loop exit makes the compiler copy the O accumulators between
+  // register sets every tile); a tile past kmax is fully masked for every
+  // lane, so its maximum is -inf, the reference stays, alpha = 1 and every
+  // probability is 0: it changes nothing
+  const int ntiles = ((kmax + C::TK - 1) / C::TK + 1) & ~1;
 
   const __bf16* Kh = p.K + (size_t)bh * p.Nkv * D;
   const __bf16* Vh = p.V + (size_t)bh * p.Nkv * D;
   // this lane's part of every tile load: row r = ROWS_PER_LOAD*(w + NW*j) + l/CH, chunk l%CH
+  // (32-bit byte offsets into the head's K or V: a head holds < 2^31 bytes)
   const int lrow0 = l / C::CH, lchunk = l % C::CH;
-  auto issue = [&](int t, unsigned char* slot) {
+  const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(Kh, p.Nkv * D * 2), vres = buffer_rsrc(Vh, p.Nkv * D * 2);
+  auto issue = [&](__amdgpu_buffer_rsrc_t res, int t, unsigned char* slot) {
     const int base = t * C::TK;
 #pragma unroll
     for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
       const int li = w + C::NW * j;
       const int r = C::ROWS_PER_LOAD * li + lrow0;
       const int key = s_idx[min(base + r, p.k - 1)];
-      const size_t off = (size_t)key * D + ((lchunk ^ swz<D>(r)) * 8);
-      dma16(Kh + off, slot + li * 1024);
-      dma16(Vh + off, slot + C::TENSOR_BYTES + li * 1024);
+      dma16_buf(res, key * (2 * D) + ((lchunk ^ swz<D>(r)) * 16), slot + li * 1024);
     }
   };
-  auto compute = [&](int t, const unsigned char* slot) {
-    st.template blocks<1, 0>(slot, slot + C::TENSOR_BYTES, vcount - t * C::TK, p.c_log2);
-  };
-
-  if (ntiles > 0) issue(0, slot0);
+  f32x16 sa[1], sb[1];
+  if (ntiles > 0) {
+    issue(kres, 0, k0);
+    issue(vres, 0, v0);
+    if (ntiles > 1) issue(kres, 1, k1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    st.template scores<1, 0>(k0, sa);
+  }
   for (int t = 0; t < ntiles; t += 2) {
+    // K(t+1) in k1, V(t) in v0, scores of tile t in sa
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, slot1);
-    compute(t, slot0);
-    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) issue(kres, t + 2, k0);
+    if (t + 1 < ntiles) issue(vres, t + 1, v1);
+    st.template step<1, 0>(sa, v0, vcount - t * C::TK, p.c_log2, k1, sb);
+    // K(t+2) in k0, V(t+1) in v1, scores of tile t+1 in sb
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 2 < ntiles) issue(t + 2, slot0);
-    compute(t + 1, slot1);
+    if (t + 3 < ntiles) issue(kres, t + 3, k1);
+    if (t + 2 < ntiles) issue(vres, t + 2, v0);
+    st.template step<1, 0>(sb, v1, vcount - (t + 1) * C::TK, p.c_log2, k0, sa);
   }
 
   float lse;
@@ -156,7 +172,7 @@ void launch_ring(const Params& p, dim3 grid, int k, hipStream_t st) {
   using C = SparseCfg<D, G>;
   const size_t lds = (size_t)k * 4;
   static const bool attr = allow_dynamic_lds((const void*)sparse_ring_kernel<D, G>,
-                                             160 * 1024 - 2 * C::SLOT_BYTES - 1024);
+                                             160 * 1024 - 4 * C::TENSOR_BYTES - 1024);
   (void)attr;
   hipLaunchKernelGGL((sparse_ring_kernel<D, G>), grid, dim3(C::NT), lds, st, p);
 }
