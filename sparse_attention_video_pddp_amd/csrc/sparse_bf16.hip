@@ -106,41 +106,49 @@ void sparse_ring_kernel(Params p) {
 
   const __bf16* Kh = p.K + (size_t)bh * p.Nkv * D;
   const __bf16* Vh = p.V + (size_t)bh * p.Nkv * D;
-  // this lane's part of every tile load: row r = ROWS_PER_LOAD*(w + NW*j) + l/CH, chunk l%CH
-  // (32-bit byte offsets into the head's K or V: a head holds < 2^31 bytes)
+  // this lane's part of every tile load: row r = ROWS_PER_LOAD*(wu + NW*j) + l/CH, chunk l%CH,
+  // as a 32-bit byte offset into the head's K or V (a head holds < 2^31 bytes); the K copy
+  // of a tile and its V copy one iteration later use the same offsets
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: LDS targets in scalar registers
   const int lrow0 = l / C::CH, lchunk = l % C::CH;
   const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(Kh, p.Nkv * D * 2), vres = buffer_rsrc(Vh, p.Nkv * D * 2);
-  auto issue = [&](__amdgpu_buffer_rsrc_t res, int t, unsigned char* slot) {
-    const int base = t * C::TK;
+  auto offsets = [&](int t, int (&o)[C::LOADS_PER_WAVE]) {
 #pragma unroll
     for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
-      const int li = w + C::NW * j;
-      const int r = C::ROWS_PER_LOAD * li + lrow0;
-      const int key = s_idx[min(base + r, p.k - 1)];
-      dma16_buf(res, key * (2 * D) + ((lchunk ^ swz<D>(r)) * 16), slot + li * 1024);
+      const int r = C::ROWS_PER_LOAD * (wu + C::NW * j) + lrow0;
+      o[j] = s_idx[min(t * C::TK + r, p.k - 1)] * (2 * D) + ((lchunk ^ swz<D>(r)) * 16);
     }
   };
+  auto issue = [&](__amdgpu_buffer_rsrc_t res, const int (&o)[C::LOADS_PER_WAVE], unsigned char* slot) {
+#pragma unroll
+    for (int j = 0; j < C::LOADS_PER_WAVE; ++j) dma16_buf(res, o[j], slot + (wu + C::NW * j) * 1024);
+  };
   f32x16 sa[1], sb[1];
+  int ok[C::LOADS_PER_WAVE], ov[C::LOADS_PER_WAVE];  // offsets of the next K copy / of the next V copy
   if (ntiles > 0) {
-    issue(kres, 0, k0);
-    issue(vres, 0, v0);
-    if (ntiles > 1) issue(kres, 1, k1);
+    offsets(0, ov);
+    issue(kres, ov, k0);
+    issue(vres, ov, v0);
+    offsets(1, ov);
+    issue(kres, ov, k1);
     wait_vmcnt<0>();
     __syncthreads();
     st.template scores<1, 0>(k0, sa);
   }
   for (int t = 0; t < ntiles; t += 2) {
-    // K(t+1) in k1, V(t) in v0, scores of tile t in sa
+    // K(t+1) in k1, V(t) in v0, scores of tile t in sa; ov = offsets of tile t+1
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 2 < ntiles) issue(kres, t + 2, k0);
-    if (t + 1 < ntiles) issue(vres, t + 1, v1);
+    offsets(t + 2, ok);
+    if (t + 2 < ntiles) issue(kres, ok, k0);
+    issue(vres, ov, v1);
     st.template step<1, 0>(sa, v0, vcount - t * C::TK, p.c_log2, k1, sb);
-    // K(t+2) in k0, V(t+1) in v1, scores of tile t+1 in sb
+    // K(t+2) in k0, V(t+1) in v1, scores of tile t+1 in sb; ok = offsets of tile t+2
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 3 < ntiles) issue(kres, t + 3, k1);
-    if (t + 2 < ntiles) issue(vres, t + 2, v0);
+    offsets(t + 3, ov);
+    if (t + 3 < ntiles) issue(kres, ov, k1);
+    if (t + 2 < ntiles) issue(vres, ok, v0);
     st.template step<1, 0>(sb, v1, vcount - (t + 1) * C::TK, p.c_log2, k0, sa);
   }
 
