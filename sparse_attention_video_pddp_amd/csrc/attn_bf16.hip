@@ -15,13 +15,11 @@
 // and the probabilities already sit in the B-operand layout of the
 // O^T = V^T P^T product (the A operand V^T comes from ds_read_b64_tr_b16).
 // Online softmax runs in base 2 with scale*log2(e) folded into one FMA.
-#include "mcs_device.hpp"
 #include "mcs_kernels.hpp"
+#include "ring.hpp"
 
 namespace mcs {
 namespace {
-
-constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int D>
 struct Tile {
@@ -271,17 +269,35 @@ struct MassParams {
   int causal_block, q_offset;
 };
 
+template <int D>
+struct MassTile {
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int RPL = 64 / CH;       // rows per wave-wide copy
+  static constexpr int LPW = 64 / RPL / 4;  // copies per wave per 64-key tile
+  static constexpr int BYTES = 64 * D * 2;
+};
+
+// K tiles of 64 keys arrive by direct-to-LDS copies in a two-slot ring (row
+// layout and swizzle of ring.hpp); one barrier per tile, which also orders the
+// per-wave column sums of the previous tile (double-buffered) before their
+// reduction over the group's waves.  A tile that every query of the wave sees
+// in full takes the unmasked path.  Three waves per SIMD: within 168
+// registers the scores stay in VGPRs (no accumulator-register copies, which
+// would cost VALU issue slots).
 template <int D, int G>
-__global__ __launch_bounds__(256) void mass_bf16_kernel(MassParams p) {
-  constexpr int NT = 256, QR = 128, GPW = QR / G, WPG = G / 32, NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * Tile<D>::KS];
-  __shared__ float part[4][64];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void mass_bf16_kernel(MassParams p) {
+  using T = MassTile<D>;
+  constexpr int QR = 128, GPW = QR / G, WPG = G / 32, NKS = D / 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[T::BYTES];
+  __shared__ float part[2][4][64];
   __shared__ int s_kmax[4];
   const int unit = xcd_unit(blockIdx.x, p.per_xcd);
   if (unit >= p.n_units) return;
   const int bhl = unit / p.upb, u = unit - bhl * p.upb;
   const int bh = p.bh0 + bhl;
   const int w = wave_id(), l = lane_id(), n = l & 31, h = l >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int pos0 = u * QR + w * 32;
   const int32_t* hperm = p.perm + (size_t)bh * p.Nq;
   const float* hlse = p.lse + (size_t)bh * p.Nq;
@@ -296,9 +312,10 @@ __global__ __launch_bounds__(256) void mass_bf16_kernel(MassParams p) {
       qa[ks] = v ? *(const bf16x8*)(qp + ks * 16) : z;
     }
   }
+  // per score row i of this lane: query 8*(i/4) + 4*h + i%4 of the wave
   float lse2[16];
   int lim[16];
-  int lmax = 0;
+  int lmax = 0, lmin = p.Nkv;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int qp = pos0 + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -307,60 +324,96 @@ __global__ __launch_bounds__(256) void mass_bf16_kernel(MassParams p) {
       const float ls = hlse[row];
       lse2[i] = (ls == -kInf) ? kInf : ls * kLog2e;
       lim[i] = visible_limit(row, p.causal_block, p.q_offset, p.Nkv);
+      lmin = min(lmin, lim[i]);
     } else {
-      lse2[i] = kInf;
+      lse2[i] = kInf;  // exp2(-inf) = 0: padding rows add nothing
       lim[i] = 0;
     }
     lmax = max(lmax, lim[i]);
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lmax = max(lmax, __shfl_xor(lmax, o, 64));
+  for (int o = 32; o >= 1; o >>= 1) {
+    lmax = max(lmax, __shfl_xor(lmax, o, 64));
+    lmin = min(lmin, __shfl_xor(lmin, o, 64));
+  }
   if (l == 0) s_kmax[w] = lmax;
   __syncthreads();
   const int kmax = max(max(s_kmax[0], s_kmax[1]), max(s_kmax[2], s_kmax[3]));
   const int ntiles = (kmax + 63) / 64;
   const __bf16* Kh = p.K + (size_t)bh * p.Nkv * D;
-  TileStage<D, NT, false> stage;
-  const int last = p.Nkv - 1;
-  if (ntiles > 0) {
-    stage.load(Kh, nullptr, [&](int r) { return min(r, last); });
-    stage.store(Ks, nullptr);
+  const int kbase = n * (2 * D) + 16 * (h ^ swz<D>(n));
+  int voff[T::LPW];
+#pragma unroll
+  for (int j = 0; j < T::LPW; ++j) {
+    const int r = T::RPL * (wu + 4 * j) + l / T::CH;
+    voff[j] = r * (2 * D) + (((l % T::CH) ^ swz<D>(r)) * 16);
   }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // rows past the end of the head read as zeros (their keys are masked)
+  auto issue = [&](int t, unsigned char* slot) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(Kh + (size_t)t * 64 * D, (p.Nkv - t * 64) * D * 2);
+#pragma unroll
+    for (int j = 0; j < T::LPW; ++j) dma16_buf(r, voff[j], slot + (wu + 4 * j) * 1024);
+  };
+  // group sums of the tile whose per-wave sums are in part[b]
+  auto reduce = [&](int t, int b) {
+    if (threadIdx.x < GPW * 64) {
+      const int gl = threadIdx.x >> 6, key = threadIdx.x & 63;
+      float m = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WPG; ++ww) m += part[b][gl * WPG + ww][key];
+      const int gg = u * GPW + gl;
+      if (gg < p.c && t * 64 + key < p.Nkv) p.mass[((size_t)bhl * p.c + gg) * p.Nkv + t * 64 + key] = m;
+    }
+  };
+  auto tile = [&](int t, const unsigned char* Ks, int b) {
     const int base = t * 64;
-    const bool more = t + 1 < ntiles;
-    if (more) stage.load(Kh, nullptr, [&](int r) { return min(base + 64 + r, last); });
+    const bool full = base + 64 <= lmin;  // every key of the tile visible to every query of the wave
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = {};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 b = *(const bf16x8*)(Ks + (kb * 32 + n) * Tile<D>::KS + ks * 16 + 8 * h);
-        s = mfma_32x32x16(qa[ks], b, s);
+        const bf16x8 kk = *(const bf16x8*)(Ks + kb * 32 * 2 * D + (kbase ^ (32 * ks)));
+        s = mfma_32x32x16(qa[ks], kk, s);
       }
-      const int key = base + kb * 32 + n;
       float cs = 0.f;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[i], p.c_log2, -lse2[i]));
-        cs += (key < lim[i]) ? pv : 0.f;
+        for (int i = 0; i < 16; ++i) cs += fast_exp2(fmaf(s[i], p.c_log2, -lse2[i]));
+      } else {
+        const int key = base + kb * 32 + n;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(fmaf(s[i], p.c_log2, -lse2[i]));
+          cs += (key < lim[i]) ? pv : 0.f;
+        }
       }
       cs += partner32(cs);
-      if (h == 0) part[w][kb * 32 + n] = cs;
+      if (h == 0) part[b][w][kb * 32 + n] = cs;
     }
-    __syncthreads();
-    if (threadIdx.x < GPW * 64) {
-      const int gl = threadIdx.x >> 6, key = threadIdx.x & 63;
-      float m = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < WPG; ++ww) m += part[gl * WPG + ww][key];
-      const int gg = u * GPW + gl;
-      if (gg < p.c && base + key < p.Nkv) p.mass[((size_t)bhl * p.c + gg) * p.Nkv + base + key] = m;
-    }
-    if (more) stage.store(Ks, nullptr);
-    __syncthreads();
+  };
+  if (ntiles > 0) {
+    issue(0, k0);
+    if (ntiles > 1) issue(1, k1);
   }
+  for (int t = 0; t < ntiles; t += 2) {
+    // K(t) landed; K(t+1), issued after it, may still be in flight
+    if (t + 1 < ntiles) wait_vmcnt<T::LPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (t > 0) reduce(t - 1, 1);
+    tile(t, k0, 0);
+    if (t + 1 >= ntiles) break;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 2 < ntiles) issue(t + 2, k0);
+    reduce(t, 0);
+    tile(t + 1, k1, 1);
+    __syncthreads();
+    if (t + 3 < ntiles) issue(t + 3, k1);
+  }
+  __syncthreads();
+  if (ntiles > 0) reduce(ntiles - 1, (ntiles - 1) & 1);
 }
 
 template <typename P>
