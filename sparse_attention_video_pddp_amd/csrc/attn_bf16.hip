@@ -28,24 +28,28 @@ struct Tile {
   static constexpr int CH = D / 8;   // 16-byte chunks per row
 };
 
-// Register staging of one 64-key tile: global -> registers -> LDS.
-template <int D, int NT, bool WITH_V>
+// Register staging of one 64-key tile: global -> registers -> LDS.  Loads are
+// buffer loads over the tile's rows: the per-thread byte offsets never change
+// (no address arithmetic per tile) and rows past the end of the head read as
+// zeros (their keys are masked).
+template <int D, int NT>
 struct TileStage {
   static constexpr int CH = D / 8;
   static constexpr int N = 64 * CH / NT;
   static_assert(N >= 1 && (64 * CH) % NT == 0, "tile/thread mismatch");
   u32x4 kr[N];
-  u32x4 vr[WITH_V ? N : 1];
+  u32x4 vr[N];
 
-  template <typename RowFn>
-  __device__ __forceinline__ void load(const __bf16* K, const __bf16* V, RowFn row) {
+  __device__ __forceinline__ void load(const __bf16* K, const __bf16* V, int row0, int nrows) {
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(K + (size_t)row0 * D, nrows * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(V + (size_t)row0 * D, nrows * D * 2);
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int ci = t + i * NT;
-      const size_t off = (size_t)row(ci / CH) * D + (ci % CH) * 8;
-      kr[i] = *(const u32x4*)(K + off);
-      if constexpr (WITH_V) vr[i] = *(const u32x4*)(V + off);
+      const int off = (ci / CH) * (2 * D) + (ci % CH) * 16;
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   }
   __device__ __forceinline__ void store(__bf16* Ks, __bf16* Vs) {
@@ -55,7 +59,7 @@ struct TileStage {
       const int ci = t + i * NT;
       const int r = ci / CH, col = (ci % CH) * 8;
       *(u32x4*)(Ks + r * Tile<D>::KS + col) = kr[i];
-      if constexpr (WITH_V) *(u32x4*)(Vs + r * Tile<D>::VS + col) = vr[i];
+      *(u32x4*)(Vs + r * Tile<D>::VS + col) = vr[i];
     }
   }
 };
@@ -117,17 +121,17 @@ struct Flash {
     const float m_ref = (m_new == -kInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_ref);
     m_run = m_new;
-    float ls = 0.f;
+    float ls4[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
     bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = fast_exp2(fmaf(s[kb][i], c, -m_ref));
-        ls += p;
+        ls4[i & 3] += p;
         pb[kb][i >> 3][i & 7] = (__bf16)p;
       }
-    l_run = fmaf(l_run, alpha, ls);
+    l_run = fmaf(l_run, alpha, (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b] *= alpha;
@@ -227,15 +231,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const __bf16* Vh = p.V + (size_t)bh * p.Nkv * D;
   Flash<D> st;
   st.init(p.Q + ((size_t)bh * p.Nq + (qv ? q : 0)) * D, qv);
-  TileStage<D, NT, true> stage;
-  const int last = p.Nkv - 1;
-  stage.load(Kh, Vh, [&](int r) { return min(r, last); });
+  TileStage<D, NT> stage;
+  stage.load(Kh, Vh, 0, p.Nkv);
   stage.store(Ks, Vs);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int base = t * 64;
     const bool more = t + 1 < ntiles;
-    if (more) stage.load(Kh, Vh, [&](int r) { return min(base + 64 + r, last); });
+    if (more) stage.load(Kh, Vh, base + 64, p.Nkv - base - 64);
     st.tile(Ks, Vs, vcount - base, p.c);
     __syncthreads();
     if (more) {
