@@ -63,6 +63,9 @@ mcs_status check_problem(const mcs_problem* p, Checked& out) {
   const long long bh = (long long)p->B * p->H;
   const long long nmax = p->Nq > p->Nkv ? p->Nq : p->Nkv;
   if (bh * nmax * p->d >= (1LL << 40)) return fail(MCS_ERR_UNSUPPORTED, "tensor sizes exceed 2^40 elements");
+  // K and V rows of one head are addressed with 32-bit byte offsets (buffer loads)
+  if ((long long)p->Nkv * p->d * 4 > 0x7fffffffLL)
+    return fail(MCS_ERR_UNSUPPORTED, "Nkv=%d: one head's K or V exceeds 2^31 bytes", p->Nkv);
   const int c = (p->Nq + p->group_size - 1) / p->group_size;
   out.s = mcs::Shape{(int)bh,  p->Nq, p->Nkv, p->d, p->group_size, p->k, c, p->scale, p->causal_block,
                      p->q_offset, p->pddp_iters};
