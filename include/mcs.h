@@ -56,7 +56,8 @@ typedef enum mcs_dtype { MCS_F32 = 0, MCS_BF16 = 1 } mcs_dtype;
 typedef enum mcs_workspace_kind { MCS_WS_GROUP = 0, MCS_WS_ANCHOR = 1 } mcs_workspace_kind;
 
 /* Problem description.  Supported: d in {64,128}; group_size in {64,128};
- * 1 <= k <= Nkv; Nq, Nkv <= 2^24; Nkv*d*4 < 2^31 (one head's K or V is
+ * 1 <= k <= Nkv, and k <= 28672 for bf16 (a group's kept-key list is held
+ * on chip); Nq, Nkv <= 2^24; Nkv*d*4 < 2^31 (one head's K or V is
  * addressed with 32-bit byte offsets); B*H*max(Nq,Nkv)*d < 2^40.  Others
  * return MCS_ERR_UNSUPPORTED or MCS_ERR_INVALID_ARG before any launch. */
 typedef struct mcs_problem {

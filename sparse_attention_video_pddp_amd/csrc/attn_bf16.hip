@@ -113,7 +113,7 @@ struct Flash {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, partner32(mx)) * c;
+    mx = half_max(mx) * c;
     // Lazy rescaling: keep the reference maximum unless this tile exceeds it
     // by more than 2^8 (probabilities stay <= 256, far from fp32/bf16 limits;
     // the final normalisation by the row sum makes the result exact).
@@ -155,7 +155,7 @@ struct Flash {
 
   // 1 / row sum (0 for a row with no visible key) and the natural-log lse.
   __device__ __forceinline__ float finish(float& lse) {
-    const float lt = l_run + partner32(l_run);
+    const float lt = half_sum(l_run);
     lse = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -kInf;
     return lt > 0.f ? 1.f / lt : 0.f;
   }
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
           cs += (key < lim[i]) ? pv : 0.f;
         }
       }
-      cs += partner32(cs);
+      cs = half_sum(cs);
       if (h == 0) part[b][w][kb * 32 + n] = cs;
     }
   };

@@ -63,6 +63,9 @@ mcs_status check_problem(const mcs_problem* p, Checked& out) {
   const long long bh = (long long)p->B * p->H;
   const long long nmax = p->Nq > p->Nkv ? p->Nq : p->Nkv;
   if (bh * nmax * p->d >= (1LL << 40)) return fail(MCS_ERR_UNSUPPORTED, "tensor sizes exceed 2^40 elements");
+  // the gathered attention keeps a group's key list in LDS next to its K/V ring
+  if (p->dtype == MCS_BF16 && p->k > mcs::kMaxKeysPerGroup)
+    return fail(MCS_ERR_UNSUPPORTED, "k=%d exceeds %d kept keys per group", p->k, mcs::kMaxKeysPerGroup);
   // K and V rows of one head are addressed with 32-bit byte offsets (buffer loads)
   if ((long long)p->Nkv * p->d * 4 > 0x7fffffffLL)
     return fail(MCS_ERR_UNSUPPORTED, "Nkv=%d: one head's K or V exceeds 2^31 bytes", p->Nkv);

@@ -42,6 +42,18 @@ __device__ __forceinline__ float partner32(float x) {
   return __uint_as_float((lane_id() & 32) ? r[0] : r[1]);
 }
 
+// max / sum of a lane's value and its partner's (lane l^32).  The swap
+// returns the low-half value in r[0] and the high-half value in r[1] on every
+// lane, so no select is needed, and both halves get the same bits.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposing 8-byte LDS read (see the layout note above).

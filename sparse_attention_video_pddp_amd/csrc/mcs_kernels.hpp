@@ -6,6 +6,10 @@
 
 namespace mcs {
 
+// Largest k the bf16 gathered attention supports (its per-group key list
+// lives in LDS beside the K/V tile ring).
+constexpr int kMaxKeysPerGroup = 28672;
+
 // Validated problem, flattened for the launchers.
 struct Shape {
   int BH;        // B * H

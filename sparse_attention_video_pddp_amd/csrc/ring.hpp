@@ -126,7 +126,7 @@ struct FlashCore {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, partner32(mx)) * c;
+    mx = half_max(mx) * c;
     const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
     const float m_ref = (m_new == -kInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_ref);
@@ -186,7 +186,7 @@ struct FlashCore {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, partner32(mx)) * c;
+    mx = half_max(mx) * c;
     const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
     const float m_ref = (m_new == -kInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_ref);
@@ -231,7 +231,7 @@ struct FlashCore {
 
   // 1 / row sum (0 for a row with no visible key) and the natural-log lse.
   __device__ __forceinline__ float finish(float& lse) const {
-    const float lt = l_run + partner32(l_run);
+    const float lt = half_sum(l_run);
     lse = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -kInf;
     return lt > 0.f ? 1.f / lt : 0.f;
   }

@@ -22,6 +22,11 @@
 namespace mcs {
 namespace {
 
+// Entries of the per-group offset table: k rounded up to a whole number of
+// 64-key tile pairs, plus one more pair (the loop reads the offsets of up to
+// two tiles past the last).
+__host__ __device__ constexpr int pad_keys(int k) { return (k + 63) / 64 * 64 + 64; }
+
 template <int D, int G>
 struct SparseCfg {
   static constexpr int NW = G / 32;
@@ -54,7 +59,7 @@ void sparse_ring_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TENSOR_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TENSOR_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TENSOR_BYTES];
-  extern __shared__ __attribute__((aligned(16))) int s_idx[];
+  extern __shared__ __attribute__((aligned(16))) int s_off[];
   __shared__ int s_kmax[C::NW];
 
   const int unit = xcd_unit(blockIdx.x, p.per_xcd);
@@ -63,8 +68,11 @@ void sparse_ring_kernel(Params p) {
   const int w = wave_id(), l = lane_id(), n = l & 31;
   const int klast = p.Nkv - 1;
   {
+    // byte offsets of the selected rows, padded with the last one so that the
+    // copies of every tile (and of the two tiles past the end) read in bounds
     const int32_t* gidx = p.idx + ((size_t)bh * p.c + g) * p.k;
-    for (int i = threadIdx.x; i < p.k; i += C::NT) s_idx[i] = min(max(gidx[i], 0), klast);
+    const int kpad = pad_keys(p.k);
+    for (int i = threadIdx.x; i < kpad; i += C::NT) s_off[i] = min(max(gidx[min(i, p.k - 1)], 0), klast) * (2 * D);
   }
   const int gsize = min(G, p.Nq - g * G);
   const int qloc = w * 32 + n;
@@ -79,10 +87,11 @@ void sparse_ring_kernel(Params p) {
   if (qv && p.causal_block) {
     const long long lim64 = ((long long)(p.q_offset + qrow) / p.causal_block + 1) * p.causal_block;
     const int lim = lim64 < p.Nkv ? (int)lim64 : p.Nkv;
+    const int lim_off = lim * (2 * D);
     int lo = 0, hi = p.k;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (s_idx[mid] < lim) lo = mid + 1; else hi = mid;
+      if (s_off[mid] < lim_off) lo = mid + 1; else hi = mid;
     }
     vcount = lo;
   }
@@ -116,7 +125,7 @@ void sparse_ring_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
       const int r = C::ROWS_PER_LOAD * (wu + C::NW * j) + lrow0;
-      o[j] = s_idx[min(t * C::TK + r, p.k - 1)] * (2 * D) + ((lchunk ^ swz<D>(r)) * 16);
+      o[j] = s_off[t * C::TK + r] | ((lchunk ^ swz<D>(r)) * 16);
     }
   };
   auto issue = [&](__amdgpu_buffer_rsrc_t res, const int (&o)[C::LOADS_PER_WAVE], unsigned char* slot) {
@@ -178,7 +187,7 @@ void sparse_ring_kernel(Params p) {
 template <int D, int G>
 void launch_ring(const Params& p, dim3 grid, int k, hipStream_t st) {
   using C = SparseCfg<D, G>;
-  const size_t lds = (size_t)k * 4;
+  const size_t lds = (size_t)pad_keys(k) * 4;
   static const bool attr = allow_dynamic_lds((const void*)sparse_ring_kernel<D, G>,
                                              160 * 1024 - 4 * C::TENSOR_BYTES - 1024);
   (void)attr;

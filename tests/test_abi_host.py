@@ -55,6 +55,7 @@ def base(**kw):
     (dict(pddp_iters=5000), mcs.MCS_ERR_INVALID_ARG),
     (dict(B=300, H=300), mcs.MCS_ERR_UNSUPPORTED),
     (dict(Nkv=1 << 22, k=60), mcs.MCS_ERR_UNSUPPORTED),   # one head's K > 2^31 bytes (32-bit offsets)
+    (dict(Nkv=40000, k=28673), mcs.MCS_ERR_UNSUPPORTED),  # kept-key list larger than the on-chip table
 ])
 def test_bad_problem_is_rejected_before_launch(kw, code):
     p = base(**kw)
