@@ -127,7 +127,10 @@ struct BlockSelect {
       const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
       const uint32_t dmask = pass == 2 ? 0xFFu : 0xFFFu;
       stripes(0, nstripes, keys, [&](int, int, uint32_t u) {
-        if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1);
+        const bool m = (u & pmask) == prefix;
+        if (__ballot(m)) {  // later passes: most stripes hold no matching key
+          if (m) atomicAdd(&sh.hist[(u >> shift) & dmask], 1);
+        }
       });
       __syncthreads();
       int cnt[BPT], local = 0;
@@ -161,13 +164,17 @@ struct BlockSelect {
     tie_need = krem;
   }
 
+  // Set bits of a wave mask held by lanes below this one.
+  static __device__ __forceinline__ int below_count(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  }
+
   // emit(stripe, j, selected, pos) for every element j < n: pos is the rank
   // of j among the selected elements, or among the remaining ones, in index
   // order.
   template <class Keys, class Emit>
   __device__ void split(const Keys& keys, uint32_t T, int tie_need, Shared& sh, Emit&& emit) const {
     const int w = wave_id(), l = lane_id();
-    const uint64_t below = (1ull << l) - 1ull;  // lanes with a lower index
     const int nstripes = VPT > 0 ? VPT : (n + NT - 1) / NT;
     int base_eq = 0, base_sel = 0;
     for (int s0 = 0; s0 < nstripes; s0 += VB) {
@@ -199,13 +206,14 @@ struct BlockSelect {
       const int my_eo = l < s1 - s0 ? sh.cnt_eq[l * NW + w] : 0;
       const int my_so = l < s1 - s0 ? sh.cnt_gt[l * NW + w] : 0;
       stripes(s0, s1, keys, [&](int s, int j, uint32_t u) {
-        const bool g = u > T, q = u == T;
-        const uint64_t eqm = __ballot(q);
-        const int eo = __builtin_amdgcn_readlane(my_eo, s - s0);  // ties before this stripe's wave slice
+        bool sel = u > T;
+        const uint64_t eqm = __ballot(u == T);
+        if (eqm) {  // rare: keys equal to T, taken lowest index first
+          const int eo = __builtin_amdgcn_readlane(my_eo, s - s0);  // ties before this stripe's wave slice
+          sel = sel || (u == T && eo + below_count(eqm) < tie_need);
+        }
         const int so = __builtin_amdgcn_readlane(my_so, s - s0);  // selections before it
-        const bool sel = g || (q && eo + __popcll(eqm & below) < tie_need);
-        const uint64_t selm = __ballot(sel);
-        const int before = so + __popcll(selm & below);  // selected elements with a lower index
+        const int before = so + below_count(__ballot(sel));       // selected elements with a lower index
         if (j < n) emit(s, j, sel, sel ? before : j - before);
       });
       base_eq += eq_tot;
