@@ -161,3 +161,33 @@ def test_single_group_and_single_key_edges(cuda):
     R = st.R[0, 0]
     sp = (Os[0, 0].float() - R)
     assert (sp - V[0, 0, j].float()).abs().max().item() <= 2e-2
+
+
+def test_side_stream_gives_the_default_stream_results(cuda):
+    """Every entry point enqueues on the stream it is given: the whole anchor
+    + reuse sequence on a side stream (default priority) matches the same
+    sequence on the default stream bit for bit, and waiting on that stream
+    alone makes the results visible."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    w = SMALL["bidir_small"]
+    p = mcs.problem_for(w)
+    (Q, K, V), _ = device_inputs(w, 0)
+    (Q1, K1, V1), _ = device_inputs(w, 1)
+
+    def run(stream):
+        st = mcs.MCSparseAttention(p)
+        with torch.cuda.stream(stream):
+            O0 = st.step(Q, K, V, True, stream=stream).clone()
+            O1 = st.step(Q1, K1, V1, False, stream=stream).clone()
+            Od = torch.empty_like(Q)
+            mcs.dense_attn(p, Q1, K1, V1, Od, stream=stream)
+        stream.synchronize()
+        return st.perm, st.idx, st.R, O0, O1, Od
+
+    torch.cuda.synchronize()
+    ref = run(torch.cuda.current_stream())
+    side = run(torch.cuda.Stream())
+    for a, b in zip(ref, side):
+        assert torch.equal(a, b)
