@@ -42,6 +42,7 @@ namespace {
 
 constexpr int kNodeThreads = 256;
 constexpr int kSplitThreads = 512;
+constexpr int kSplitWideThreads = 1024;  // nodes of 32769..81920 rows: 80 keys per thread
 constexpr int kProjRows = 512;      // rows per workgroup of the projection kernel
 constexpr int kMaxChunkRows = 4096;  // row chunk of the many-workgroup levels; larger nodes split there
 
@@ -528,9 +529,9 @@ __global__ __launch_bounds__(256) void pddp_project_kernel(PddpParams p) {
                              [&](int i, uint32_t k) { nkeys[i] = k; });
 }
 
-template <int VPT>
-__global__ __launch_bounds__(kSplitThreads) void pddp_split_kernel(PddpParams p) {
-  using Sel = BlockSelect<kSplitThreads, VPT>;
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT) void pddp_split_kernel(PddpParams p) {
+  using Sel = BlockSelect<NT, VPT>;
   __shared__ typename Sel::Shared sh;
   const int bh = blockIdx.y;
   const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
@@ -555,26 +556,26 @@ __global__ __launch_bounds__(kSplitThreads) void pddp_split_kernel(PddpParams p)
   __syncthreads();
   int32_t* staged = (int32_t*)(p.keys + off);
   constexpr int U = 8;
-  for (int i0 = 0; i0 < nd.n; i0 += U * kSplitThreads) {
+  for (int i0 = 0; i0 < nd.n; i0 += U * NT) {
     int src[U], val[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) src[u] = ntmp[min(i0 + u * kSplitThreads + (int)threadIdx.x, nd.n - 1)];
+    for (int u = 0; u < U; ++u) src[u] = ntmp[min(i0 + u * NT + (int)threadIdx.x, nd.n - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u) val[u] = nperm[min(max(src[u], 0), nd.n - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kSplitThreads + (int)threadIdx.x;
+      const int i = i0 + u * NT + (int)threadIdx.x;
       if (i < nd.n) staged[i] = val[u];
     }
   }
   __syncthreads();
-  for (int i0 = 0; i0 < nd.n; i0 += U * kSplitThreads) {
+  for (int i0 = 0; i0 < nd.n; i0 += U * NT) {
     int val[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) val[u] = staged[min(i0 + u * kSplitThreads + (int)threadIdx.x, nd.n - 1)];
+    for (int u = 0; u < U; ++u) val[u] = staged[min(i0 + u * NT + (int)threadIdx.x, nd.n - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kSplitThreads + (int)threadIdx.x;
+      const int i = i0 + u * NT + (int)threadIdx.x;
       if (i < nd.n) nperm[i] = val[u];
     }
   }
@@ -634,9 +635,12 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
       p.pj_pmax = (int)((maxn + kProjRows - 1) / kProjRows);
       hipLaunchKernelGGL((pddp_project_kernel<D, BF16>), dim3(nslots * p.pj_pmax, s.BH), dim3(256), 0, st, p);
       if (maxn <= 64LL * kSplitThreads)
-        hipLaunchKernelGGL((pddp_split_kernel<64>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 64>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+      else if (maxn <= 80LL * kSplitWideThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 80>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
+                           st, p);
       else
-        hipLaunchKernelGGL((pddp_split_kernel<0>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 0>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
     } else {
       const dim3 grid(nslots, s.BH);
       static_assert(kMaxChunkRows <= 16 * kNodeThreads, "node kernel register cache");

@@ -11,7 +11,7 @@
 // Element j of the array belongs to thread j % NT ("stripe" j / NT).  With
 // VPT > 0 the caller caches the keys of its VPT stripes in registers (the
 // array must then hold at most VPT * NT elements); with VPT == 0 keys are
-// re-read through a functor on every pass.  Positions j >= n of the last
+// re-read through a functor on every pass (four reads in all).  Positions j >= n of the last
 // stripe read as key 0: they sit above every real index, so they are never
 // selected ahead of a real key (at most n are selected) and every stripe can
 // be processed without lane masks; only the final emit skips them.
@@ -60,7 +60,7 @@ struct BlockSelect {
   static constexpr int NBIN = 4096;
   static constexpr int BPT = NBIN / NT;  // histogram bins owned by one thread in the rank search
   static constexpr int VB = 64;         // stripes per split block (one per lane; VB * NW <= NT)
-  static_assert(VPT >= 0 && VPT <= VB, "register cache");
+  static_assert(VPT >= 0, "register cache");
 
   struct Shared {
     int hist[NBIN];
@@ -92,15 +92,16 @@ struct BlockSelect {
   }
 
   // f(stripe, j, key) for the stripes [s0, s1) of this thread (uniform trip
-  // count; in register mode always all VPT stripes, s0 = 0 and s1 = VPT).
+  // count).  In register mode s0 and s1 are compile-time after unrolling
+  // (whole blocks of VB stripes, also those past the end, keys 0 — see
+  // above), so no per-stripe conditions stay live.
   template <class Keys, class F>
   __device__ __forceinline__ void stripes(int s0, int s1, const Keys& keys, F&& f) const {
     const int t = threadIdx.x;
     if constexpr (VPT > 0) {
-      // all VPT stripes, also those past the end (keys 0, see above): no
-      // per-stripe conditions to keep live
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) f(i, i * NT + t, v[i]);
+      for (int i = 0; i < VPT; ++i)
+        if (i >= s0 && i < s1) f(i, i * NT + t, v[i]);
     } else {
       for (int s = s0; s < s1; ++s) {
         const int j = s * NT + t;
@@ -177,8 +178,7 @@ struct BlockSelect {
     const int w = wave_id(), l = lane_id();
     const int nstripes = VPT > 0 ? VPT : (n + NT - 1) / NT;
     int base_eq = 0, base_sel = 0;
-    for (int s0 = 0; s0 < nstripes; s0 += VB) {
-      const int s1 = min(nstripes, s0 + VB);
+    auto block = [&](int s0, int s1) {
       // lane i of each wave collects the counts of stripe s0 + i (VB == 64 lanes)
       int my_gt = 0, my_eq = 0;
       stripes(s0, s1, keys, [&](int s, int, uint32_t u) {
@@ -218,7 +218,13 @@ struct BlockSelect {
       });
       base_eq += eq_tot;
       base_sel += sel_tot;
-      if (s1 < nstripes) __syncthreads();
+      if (s1 < nstripes) __syncthreads();  // the counts are reused by the next block
+    };
+    if constexpr (VPT > 0) {
+#pragma unroll
+      for (int s0 = 0; s0 < VPT; s0 += VB) block(s0, s0 + VB < VPT ? s0 + VB : VPT);
+    } else {
+      for (int s0 = 0; s0 < nstripes; s0 += VB) block(s0, min(nstripes, s0 + VB));
     }
   }
 };

@@ -6,8 +6,9 @@
 // non-negative floats, so their bit patterns order like the values (a -0 is
 // read as +0).  The block select (select.hpp) finds the k-th largest pattern
 // and emits the kept keys in ascending index order, equal masses taken
-// lowest index first.  Rows of up to 32768 keys are held in registers (64
-// per thread, one HBM read); longer rows are re-read on each pass.
+// lowest index first.  Rows of up to 81920 keys are held in registers (up to
+// 64 keys per thread of a 512-thread workgroup, or 80 of a 1024-thread one;
+// one HBM read); longer rows are re-read on each pass.
 #include "mcs_kernels.hpp"
 #include "select.hpp"
 
@@ -15,6 +16,7 @@ namespace mcs {
 namespace {
 
 constexpr int kTopkThreads = 512;
+constexpr int kTopkWideThreads = 1024;  // rows of 32769..81920 keys: 80 per thread
 
 struct TopkParams {
   const float* mass;
@@ -30,9 +32,9 @@ struct MassKeys {
   }
 };
 
-template <int VPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  using Sel = BlockSelect<kTopkThreads, VPT>;
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
+  using Sel = BlockSelect<NT, VPT>;
   __shared__ typename Sel::Shared sh;
   const int unit = blockIdx.x;
   const int bhl = unit / p.c, g = unit - bhl * p.c;
@@ -49,9 +51,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   });
 }
 
-template <int VPT>
+template <int NT, int VPT>
 void launch(const TopkParams& p, int rows, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel<VPT>, dim3(rows), dim3(kTopkThreads), 0, st, p);
+  hipLaunchKernelGGL((topk_kernel<NT, VPT>), dim3(rows), dim3(NT), 0, st, p);
 }
 
 }  // namespace
@@ -59,10 +61,11 @@ void launch(const TopkParams& p, int rows, hipStream_t st) {
 hipError_t launch_topk(const Shape& s, int bh0, int nbh, const float* mass, int32_t* idx, hipStream_t st) {
   const TopkParams p{mass, idx, s.Nkv, s.k, s.c, bh0};
   const int rows = nbh * s.c;
-  if (s.Nkv <= 4 * kTopkThreads) launch<4>(p, rows, st);
-  else if (s.Nkv <= 16 * kTopkThreads) launch<16>(p, rows, st);
-  else if (s.Nkv <= 64 * kTopkThreads) launch<64>(p, rows, st);
-  else launch<0>(p, rows, st);
+  if (s.Nkv <= 4 * kTopkThreads) launch<kTopkThreads, 4>(p, rows, st);
+  else if (s.Nkv <= 16 * kTopkThreads) launch<kTopkThreads, 16>(p, rows, st);
+  else if (s.Nkv <= 64 * kTopkThreads) launch<kTopkThreads, 64>(p, rows, st);
+  else if (s.Nkv <= 80 * kTopkWideThreads) launch<kTopkWideThreads, 80>(p, rows, st);
+  else launch<kTopkThreads, 0>(p, rows, st);
   return hipGetLastError();
 }
 
