@@ -109,6 +109,22 @@ __device__ __forceinline__ double partner32_f64(double x) {
   return __longlong_as_double((long long)(((unsigned long long)h << 32) | l));
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// fp32 sum over the 64 lanes, returned in every lane (same pattern as below).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16, 64);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the 64 lanes, returned in every lane: DPP within rows of 16
 // (quad swaps, half-row and row mirrors), then the row pairs and the halves.
 __device__ __forceinline__ double wave_sum_f64(double v) {

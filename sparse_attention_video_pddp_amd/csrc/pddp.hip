@@ -435,6 +435,198 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   });
 }
 
+// ---- small nodes ------------------------------------------------------------
+// Nodes of at most kSmallRows rows (the deep levels: thousands of nodes, each a
+// chain of latencies) run with a lighter state so that four workgroups share a
+// CU: the scatter sums of all tiles stay in the fp32 MFMA accumulators (exact
+// bf16 products, fp32 sums over at most kSmallRows rows), the centring is
+// done in fp64 and the power iteration runs in fp32 (C rounded to fp32); the
+// projections stay fp64.  K tiles of 32 rows in a two-slot ring of 8 KB.
+constexpr int kSmallRows = 512;
+
+template <int D>
+__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void pddp_small_kernel(PddpParams p) {
+  constexpr int NB = D / 32;
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RPL = 64 / CH;         // rows per wave-wide copy
+  constexpr int TR = 32;               // rows per tile
+  constexpr int LPW = TR / RPL / 4;    // wave-wide copies per wave per tile
+  constexpr int TILE = TR * D * 2;
+  constexpr int VPT = kSmallRows / kNodeThreads;
+  static_assert(LPW >= 1, "tile copy split");
+  using Sel = BlockSelect<kNodeThreads, VPT>;
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[TILE];
+  __shared__ double sS[D], sV[D], sMu[4];
+  __shared__ float sY[2][D], sRed[2][4];
+  __shared__ typename Sel::Shared sh;
+  __shared__ uint32_t s_keys[kSmallRows];
+  const int bh = blockIdx.y;
+  const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
+  if (nd.c <= 1) return;
+  const size_t hbase = (size_t)bh * p.Nq;
+  int32_t* nperm = p.perm + hbase + nd.start;
+  const int n = nd.n;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool gw = w < NB;
+
+  // ---- 1. scatter sums, fp32 over all tiles ---------------------------------
+  const __bf16* Qh = (const __bf16*)p.Q + hbase * D;
+  const int vr = 4 * h + ((l & 15) >> 2);
+  const int c0 = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+  const int ob0 = vr * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(vr));
+  const int ob1 = (8 + vr) * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(8 + vr));
+  const int lrow0 = l / CH, lchunk = l % CH;
+  const int ntiles = (n + TR - 1) / TR;
+  int ids[LPW];
+  auto load_ids = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) ids[j] = nperm[min(t * TR + RPL * (wu + 4 * j) + lrow0, n - 1)];
+  };
+  auto issue = [&](unsigned char* slot) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int r = RPL * (wu + 4 * j) + lrow0;
+      dma16(Qh + (size_t)ids[j] * D + ((lchunk ^ swz<D>(r)) * 8), slot + (wu + 4 * j) * 1024);
+    }
+  };
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
+  f32x16 acc[NB], accS = {};
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+  auto compute = [&](const unsigned char* slot, int valid) {
+    if (!gw) return;
+#pragma unroll
+    for (int ks2 = 0; ks2 < TR / 16; ++ks2) {
+      const unsigned char* base = slot + 16 * (2 * D) * ks2;
+      bf16x8 op[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) op[b] = cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
+      if (valid < TR) {
+        const __bf16 z = (__bf16)0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool k0 = 16 * ks2 + 4 * h + j < valid, k1 = 16 * ks2 + 8 + 4 * h + j < valid;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            op[b][j] = k0 ? op[b][j] : z;
+            op[b][4 + j] = k1 ? op[b][4 + j] : z;
+          }
+        }
+      }
+      bf16x8 ow = op[0];
+#pragma unroll
+      for (int b = 1; b < NB; ++b) ow = (b == w) ? op[b] : ow;
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) acc[bi] = mfma_32x32x16(op[bi], ow, acc[bi]);
+      accS = mfma_32x32x16(ow, ones, accS);
+    }
+  };
+  load_ids(0);
+  issue(slot0);
+  if (ntiles > 1) load_ids(1);
+  for (int t = 0; t < ntiles; t += 2) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      issue(slot1);
+      if (t + 2 < ntiles) load_ids(t + 2);
+    }
+    compute(slot0, n - t * TR);
+    if (t + 1 >= ntiles) break;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 2 < ntiles) {
+      issue(slot0);
+      if (t + 3 < ntiles) load_ids(t + 3);
+    }
+    compute(slot1, n - (t + 1) * TR);
+  }
+  // column sums: lane (n, h) of wave w keeps element n%16: S[32w + 8((n%16)/4) + 4h + n%4]
+  {
+    const int si = ln & 15;
+    float sv = accS[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) sv = (si == i) ? accS[i] : sv;
+    if (gw && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = (double)sv;
+  }
+  __syncthreads();
+
+  // ---- 2. centre in fp64, iterate in fp32 ------------------------------------
+  const double inv_n = 1.0 / (double)n;
+  float cf[NB][16];
+  if (gw) {
+    const double sc = sS[w * 32 + ln] * inv_n;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        cf[bi][i] = (float)((double)acc[bi][i] - sS[bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)] * sc);
+  }
+  if (tid < D) sY[0][tid] = 1.0f / sqrtf((float)D);
+  if (tid < 4) sRed[0][tid] = tid == 0 ? 1.0f : 0.0f;
+  __syncthreads();
+  int cur = 0, last = 0;
+  for (int it = 0; it < p.iters; ++it) {
+    const float nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
+    if (nrm2 == 0.0f) break;  // C v = 0: keep the previous direction
+    last = cur;
+    const float inv = 1.0f / sqrtf(nrm2);
+    float wv = 0.0f;
+    if (gw) {
+      float part[NB];
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
+        part[bi] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part[bi] = fmaf(cf[bi][i], sY[cur][bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], part[bi]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) wv += part[bi];
+      wv = half_sum(wv) * inv;
+    }
+    const float sq = wave_sum_f32((gw && h == 0) ? wv * wv : 0.0f);
+    const int nxt = cur ^ 1;
+    if (gw && h == 0) sY[nxt][w * 32 + ln] = wv;
+    if (l == 0 && w < 4) sRed[nxt][w] = gw ? sq : 0.0f;
+    __syncthreads();
+    cur = nxt;
+  }
+  {
+    const float nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
+    if (nrm2 != 0.0f) last = cur;
+  }
+  const float nl = (sRed[last][0] + sRed[last][1]) + (sRed[last][2] + sRed[last][3]);
+  const double vinv = 1.0 / sqrt((double)nl);
+  if (tid < D) sV[tid] = (double)sY[last][tid] * vinv;
+  __syncthreads();
+  const double mv = wave_sum_f64(tid < D ? sS[tid] * inv_n * sV[tid] : 0.0);
+  if (l == 0 && w < 4) sMu[w] = mv;
+  __syncthreads();
+  const double muv = (sMu[0] + sMu[1]) + (sMu[2] + sMu[3]);
+
+  // ---- 3, 4. projections and split -------------------------------------------
+  project_rows<D, true, kNodeThreads>(p.Q, hbase, nperm, 0, n, sV, muv, [&](int i, uint32_t k) { s_keys[i] = k; });
+  __syncthreads();
+  Sel sel;
+  sel.n = n;
+  int mid[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) mid[i] = nperm[min(i * kNodeThreads + tid, n - 1)];
+  sel.load(LdsKeys{s_keys});
+  const int nL = (nd.c >> 1) * p.G;
+  uint32_t T;
+  int tie_need;
+  sel.threshold(NoKeys{}, nL, sh, T, tie_need);  // its barriers also retire every read of nperm
+  sel.split(NoKeys{}, T, tie_need, sh, [&](int i, int, bool s, int pos) {
+    const int dst = s ? pos : nL + pos;
+    if (dst < n) nperm[dst] = mid[i];
+  });
+}
+
 // ---- many workgroups per node ---------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void pddp_gram_kernel(PddpParams p) {
@@ -644,7 +836,9 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
     } else {
       const dim3 grid(nslots, s.BH);
       static_assert(kMaxChunkRows <= 16 * kNodeThreads, "node kernel register cache");
-      if (maxn <= 2 * kNodeThreads)
+      if (BF16 && maxn <= kSmallRows)
+        hipLaunchKernelGGL((pddp_small_kernel<D>), grid, dim3(kNodeThreads), 0, st, p);
+      else if (maxn <= 2 * kNodeThreads)
         hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 2>), grid, dim3(kNodeThreads), 0, st, p);
       else if (maxn <= 8 * kNodeThreads)
         hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 8>), grid, dim3(kNodeThreads), 0, st, p);
