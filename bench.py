@@ -176,11 +176,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
 
 def reuse_bytes_per_launch(w) -> float:
     """Algorithmic bytes of one mcs_sparse_attn call: per (b,h,group) the k
-    gathered K and V rows (bf16), the group's Q rows (bf16), R rows (fp32),
-    O rows (bf16) and the k indices (int32)."""
+    gathered K and V rows, the group's Q, R and O rows (all in the input
+    dtype) and the k indices (int32)."""
     e = 2 if w.dtype == "bf16" else 4
     BH = w.B * w.H
-    return BH * (w.n_groups * (2 * w.k * w.d * e + 4 * w.k) + w.Nq * w.d * (e + 4 + e))
+    return BH * (w.n_groups * (2 * w.k * w.d * e + 4 * w.k) + w.Nq * w.d * 3 * e)
 
 
 def dense_flops(w) -> float:

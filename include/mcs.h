@@ -22,7 +22,8 @@
  *  - Layouts are row-major: Q [B,H,Nq,d], K and V [B,H,Nkv,d], O [B,H,Nq,d]
  *    (d fastest).  Tokens of a (frames x height x width) latent are flattened
  *    frame-major, n = (t*height + y)*width + x.
- *  - Q, K, V and O have element type `dtype`; R, lse and scores are float32.
+ *  - Q, K, V, O and the residual R have element type `dtype`; lse and scores
+ *    are float32.
  *  - Query row i sits at position q_offset + i of the KV sequence.  With
  *    causal_block == 0 every key is visible; otherwise key j is visible to
  *    query i iff j / causal_block <= (q_offset + i) / causal_block
@@ -77,7 +78,9 @@ typedef struct mcs_problem {
 /* Bytes of workspace mcs_group (kind MCS_WS_GROUP) or mcs_anchor
  * (MCS_WS_ANCHOR) needs to process all B*H heads in one pass.  For
  * MCS_WS_ANCHOR any size of at least `*min_bytes` works (heads are then
- * processed in chunks); min_bytes may be NULL.  Pure host computation. */
+ * processed in chunks); min_bytes may be NULL.  For bf16 problems the anchor
+ * workspace also holds the float32 O_full of all heads (B*H*Nq*d*4 bytes, part
+ * of the minimum).  Pure host computation. */
 mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes, size_t* min_bytes);
 
 /* Fast-PDDP query grouping (MC-Sparse review, section 3: equal-size,
@@ -117,11 +120,11 @@ mcs_status mcs_dense_attn(const mcs_problem* p, const void* Q, const void* K, co
  *   perm [B,H,Nq] int32, read (a valid grouping; not checked on the device).
  *   O    [B,H,Nq,d] dtype, written with O_full (rounded to dtype).
  *   idx  [B,H,c,k] int32, written: each group's selected key indices, ascending.
- *   R    [B,H,Nq,d] float32, written (original token order; computed from the
- *        unrounded float32 O_full).
+ *   R    [B,H,Nq,d] dtype, written (original token order): O_full - O_sparse
+ *        formed in float32 from the unrounded O_full, rounded once to dtype.
  *   ws   workspace of at least the minimum mcs_workspace_size(MCS_WS_ANCHOR). */
 mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const void* V,
-                      const int32_t* perm, void* O, int32_t* idx, float* R, void* ws, size_t ws_bytes,
+                      const int32_t* perm, void* O, int32_t* idx, void* R, void* ws, size_t ws_bytes,
                       void* stream);
 
 /* Reuse step (MC-Sparse review, section 3): gathered sparse attention of each
@@ -130,10 +133,11 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
  *   O_i = sum_{j in S_g(i), visible} softmax_j(scale*<q_i,k_j>) v_j + R_i.
  *   perm, idx from the anchor (perm must be a permutation of [0,Nq) and idx
  *   values in [0,Nkv); not checked on the device).
- *   R    [B,H,Nq,d] float32 from the anchor, or NULL for plain sparse attention.
+ *   R    [B,H,Nq,d] dtype from the anchor, or NULL for plain sparse attention;
+ *        added in float32, the sum rounded once to dtype.
  *   O    [B,H,Nq,d] dtype, written (may not alias Q, K, V or R). */
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,
-                           const int32_t* perm, const int32_t* idx, const float* R, void* O,
+                           const int32_t* perm, const int32_t* idx, const void* R, void* O,
                            void* stream);
 
 /* Static description of a status code. */

@@ -115,6 +115,10 @@ mcs_status check_ptrs(std::initializer_list<Ptr> ptrs) {
 }
 
 size_t anchor_lse_bytes(const mcs::Shape& s) { return round_up((size_t)s.BH * s.Nq * 4); }
+// bf16: the float32 dense output of all heads, kept until the residual is formed
+size_t anchor_ofull_bytes(const mcs::Shape& s, bool bf16) {
+  return bf16 ? round_up((size_t)s.BH * s.Nq * s.d * 4) : 0;
+}
 size_t anchor_mass_bytes_per_head(const mcs::Shape& s) { return round_up((size_t)s.c * s.Nkv * 4); }
 
 mcs_status hip_status(hipError_t e, const char* what) {
@@ -150,8 +154,9 @@ mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes,
     need = need_min = c.empty ? 0 : mcs::pddp_workspace_bytes(c.s);
   } else if (kind == MCS_WS_ANCHOR) {
     if (!c.empty) {
-      need = anchor_lse_bytes(c.s) + (size_t)c.s.BH * anchor_mass_bytes_per_head(c.s);
-      need_min = anchor_lse_bytes(c.s) + anchor_mass_bytes_per_head(c.s);
+      const size_t fixed = anchor_lse_bytes(c.s) + anchor_ofull_bytes(c.s, c.bf16);
+      need = fixed + (size_t)c.s.BH * anchor_mass_bytes_per_head(c.s);
+      need_min = fixed + anchor_mass_bytes_per_head(c.s);
     }
   } else {
     return fail(MCS_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
@@ -188,7 +193,7 @@ mcs_status mcs_dense_attn(const mcs_problem* p, const void* Q, const void* K, co
 }
 
 mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const void* V,
-                      const int32_t* perm, void* O, int32_t* idx, float* R, void* ws, size_t ws_bytes,
+                      const int32_t* perm, void* O, int32_t* idx, void* R, void* ws, size_t ws_bytes,
                       void* stream) {
   Checked c;
   if (mcs_status s = check_problem(p, c)) return s;
@@ -196,18 +201,21 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
   if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {perm, "perm", false},
                                  {O, "O", false}, {idx, "idx", false}, {R, "R", false}, {ws, "ws", false}}))
     return s;
-  if (O == Q || O == K || O == V || (void*)R == O || (void*)R == Q || (void*)R == K || (void*)R == V)
+  if (O == Q || O == K || O == V || R == O || R == Q || R == K || R == V)
     return fail(MCS_ERR_INVALID_ARG, "an output aliases another argument");
-  const size_t lse_b = anchor_lse_bytes(c.s), head_b = anchor_mass_bytes_per_head(c.s);
-  if (ws_bytes < lse_b + head_b)
-    return fail(MCS_ERR_WORKSPACE, "anchor workspace %zu < minimum %zu bytes", ws_bytes, lse_b + head_b);
-  const size_t fit = (ws_bytes - lse_b) / head_b;
+  const size_t lse_b = anchor_lse_bytes(c.s), of_b = anchor_ofull_bytes(c.s, c.bf16);
+  const size_t head_b = anchor_mass_bytes_per_head(c.s);
+  if (ws_bytes < lse_b + of_b + head_b)
+    return fail(MCS_ERR_WORKSPACE, "anchor workspace %zu < minimum %zu bytes", ws_bytes, lse_b + of_b + head_b);
+  const size_t fit = (ws_bytes - lse_b - of_b) / head_b;
   const int chunk = fit >= (size_t)c.s.BH ? c.s.BH : (int)fit;
   float* lse = (float*)ws;
-  float* mass = (float*)((char*)ws + lse_b);
+  // bf16: O_full (float32) in the workspace; float32: straight into R
+  float* ofull = c.bf16 ? (float*)((char*)ws + lse_b) : (float*)R;
+  float* mass = (float*)((char*)ws + lse_b + of_b);
   const hipStream_t st = (hipStream_t)stream;
-  hipError_t e = c.bf16 ? mcs::launch_dense_bf16(c.s, Q, K, V, O, lse, R, st)
-                        : mcs::launch_dense_f32(c.s, Q, K, V, O, lse, R, st);
+  hipError_t e = c.bf16 ? mcs::launch_dense_bf16(c.s, Q, K, V, O, lse, ofull, st)
+                        : mcs::launch_dense_f32(c.s, Q, K, V, O, lse, ofull, st);
   if (e != hipSuccess) return hip_status(e, "mcs_anchor (dense)");
   for (int bh0 = 0; bh0 < c.s.BH; bh0 += chunk) {
     const int nbh = c.s.BH - bh0 < chunk ? c.s.BH - bh0 : chunk;
@@ -217,13 +225,13 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
     e = mcs::launch_topk(c.s, bh0, nbh, mass, idx, st);
     if (e != hipSuccess) return hip_status(e, "mcs_anchor (top-k)");
   }
-  e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, R, nullptr, true, st)
-             : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, R, nullptr, true, st);
+  e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, ofull, R, nullptr, true, st)
+             : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, (float*)R, nullptr, true, st);
   return hip_status(e, "mcs_anchor (sparse)");
 }
 
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,
-                           const int32_t* perm, const int32_t* idx, const float* R, void* O,
+                           const int32_t* perm, const int32_t* idx, const void* R, void* O,
                            void* stream) {
   Checked c;
   if (mcs_status s = check_problem(p, c)) return s;
@@ -231,10 +239,10 @@ mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, c
   if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {perm, "perm", false},
                                  {idx, "idx", false}, {R, "R", true}, {O, "O", false}}))
     return s;
-  if (O == Q || O == K || O == V || O == (const void*)R)
+  if (O == Q || O == K || O == V || O == R)
     return fail(MCS_ERR_INVALID_ARG, "O aliases an input");
   const hipStream_t st = (hipStream_t)stream;
-  const hipError_t e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, (float*)R, O, false, st)
+  const hipError_t e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, nullptr, (void*)R, O, false, st)
                               : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, (float*)R, O, false, st);
   return hip_status(e, "mcs_sparse_attn");
 }

@@ -35,11 +35,12 @@ hipError_t launch_mass_f32(const Shape& s, int bh0, int nbh, const void* Q, cons
 // Top-k per group row of `mass` (heads [bh0, bh0+nbh)), written to idx[bh][g][k] ascending.
 hipError_t launch_topk(const Shape& s, int bh0, int nbh, const float* mass, int32_t* idx, hipStream_t st);
 
-// Gathered sparse attention.  anchor: R <- R - O_sparse (R holds O_full on
-// entry).  reuse: O <- O_sparse + R (R may be null).
+// Gathered sparse attention, bf16.  anchor: R <- bf16(Ofull - O_sparse)
+// (Ofull: the float32 dense output).  reuse: O <- O_sparse + R (R may be null).
 hipError_t launch_sparse_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
-                              hipStream_t st);
+                              const int32_t* perm, const int32_t* idx, const float* Ofull, void* R, void* O,
+                              bool anchor, hipStream_t st);
+// float32: anchor: R <- R - O_sparse (R holds O_full on entry); reuse as above.
 hipError_t launch_sparse_f32(const Shape& s, const void* Q, const void* K, const void* V,
                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
                              hipStream_t st);

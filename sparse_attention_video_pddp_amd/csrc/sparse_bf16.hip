@@ -16,6 +16,13 @@
 // full iteration before it is read.  The slots are distinct LDS objects and
 // the loop is unrolled by two, so the compiler can tell the slots being read
 // from the slots being filled and adds no wait for the copies in flight.
+//
+// Residual (reuse step): R has the input dtype.  The K slots are no longer
+// needed once the last tile pair has started, so the group's first 2*TK
+// residual rows are copied into them during that pair (one slot per half);
+// the epilogue then reads them from LDS instead of waiting for HBM.  Rows
+// beyond 2*TK (G = 128) are read directly.  At the anchor, R is formed from
+// the float32 dense output in the workspace.
 #include "mcs_kernels.hpp"
 #include "ring.hpp"
 
@@ -43,7 +50,8 @@ struct SparseCfg {
 struct Params {
   const __bf16 *Q, *K, *V;
   const int32_t *perm, *idx;
-  float* R;
+  const float* Ofull;  // anchor: float32 dense output [BH, Nq, D]
+  __bf16* R;           // anchor: written; reuse: read (may be null)
   __bf16* O;
   int Nq, Nkv, k, c, n_units, per_xcd;
   float c_log2;
@@ -61,6 +69,7 @@ void sparse_ring_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TENSOR_BYTES];
   extern __shared__ __attribute__((aligned(16))) int s_off[];
   __shared__ int s_kmax[C::NW];
+  __shared__ int s_qrow[G];
 
   const int unit = xcd_unit(blockIdx.x, p.per_xcd);
   if (unit >= p.n_units) return;
@@ -80,6 +89,7 @@ void sparse_ring_kernel(Params p) {
   const int32_t* gperm = p.perm + (size_t)bh * p.Nq + (size_t)g * G;
   // caller data is not validated on the device; clamping keeps every access in bounds
   const int qrow = min(max(gperm[qv ? qloc : 0], 0), p.Nq - 1);
+  if (l < 32) s_qrow[qloc] = qrow;  // rows of the residual copies (a valid row for every slot)
   __syncthreads();
 
   // number of selected keys visible to this lane's query (a prefix: ascending list)
@@ -132,6 +142,18 @@ void sparse_ring_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < C::LOADS_PER_WAVE; ++j) dma16_buf(res, o[j], slot + (wu + C::NW * j) * 1024);
   };
+  // residual rows [TK*part, TK*part + TK) of the group into a K slot, laid out like a K tile
+  constexpr int RROWS = G < 2 * C::TK ? G : 2 * C::TK;  // rows that go through LDS
+  const bool rcopy = !p.anchor && p.R != nullptr;
+  const __bf16* Rh = rcopy ? p.R + (size_t)bh * p.Nq * D : nullptr;
+  auto issue_r = [&](int part, unsigned char* slot) {
+#pragma unroll
+    for (int j = 0; j < C::LOADS_PER_WAVE; ++j) {
+      const int r = C::ROWS_PER_LOAD * (wu + C::NW * j) + lrow0;
+      const int row = s_qrow[min(part * C::TK + r, G - 1)];
+      dma16(Rh + (size_t)row * D + (lchunk ^ swz<D>(r)) * 8, slot + (wu + C::NW * j) * 1024);
+    }
+  };
   f32x16 sa[1], sb[1];
   int ok[C::LOADS_PER_WAVE], ov[C::LOADS_PER_WAVE];  // offsets of the next K copy / of the next V copy
   if (ntiles > 0) {
@@ -145,42 +167,75 @@ void sparse_ring_kernel(Params p) {
     st.template scores<1, 0>(k0, sa);
   }
   for (int t = 0; t < ntiles; t += 2) {
+    const bool last = t + 2 >= ntiles;
     // K(t+1) in k1, V(t) in v0, scores of tile t in sa; ov = offsets of tile t+1
     wait_vmcnt<0>();
     __syncthreads();
     offsets(t + 2, ok);
-    if (t + 2 < ntiles) issue(kres, ok, k0);
+    if (!last) issue(kres, ok, k0);
+    else if (rcopy) issue_r(0, k0);  // k0 is free from here on
     issue(vres, ov, v1);
     st.template step<1, 0>(sa, v0, vcount - t * C::TK, p.c_log2, k1, sb);
     // K(t+2) in k0, V(t+1) in v1, scores of tile t+1 in sb; ok = offsets of tile t+2
     wait_vmcnt<0>();
     __syncthreads();
     offsets(t + 3, ov);
-    if (t + 3 < ntiles) issue(kres, ov, k1);
-    if (t + 2 < ntiles) issue(vres, ok, v0);
+    if (!last) {
+      issue(kres, ov, k1);
+      issue(vres, ok, v0);
+    } else if (rcopy && RROWS > C::TK) {
+      issue_r(1, k1);  // k1 is free from here on
+    }
+    // on the last pair the scores formed here (from k0) belong to no tile and are never used
     st.template step<1, 0>(sb, v1, vcount - (t + 1) * C::TK, p.c_log2, k0, sa);
+  }
+  const bool rlds = rcopy && ntiles > 0;  // residual rows [0, RROWS) are in k0/k1
+  if (rlds) {
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 
   float lse;
   const float inv = st.finish(lse);
-  if (qv) {
-    const int h = l >> 5;
-    const size_t row = ((size_t)bh * p.Nq + qrow) * D;
+  if (!qv) return;
+  const int h = l >> 5;
+  const size_t row = ((size_t)bh * p.Nq + qrow) * D;
+  // output channels d0..d0+3 of this lane: d0 = 32b + 8q4 + 4h, i.e. half h of
+  // 16-byte chunk 4b+q4 of the row
+  auto write_out = [&](auto residual) {
 #pragma unroll
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = b * 32 + 8 * q4 + 4 * h;
         f32x4 v = st.out4(b, q4, inv);
-        if (p.anchor) {
-          float* rp = p.R + row + d0;
-          *(f32x4*)rp = *(const f32x4*)rp - v;
-        } else {
-          if (p.R) v += *(const f32x4*)(p.R + row + d0);
-          bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-          *(bf16x4*)(p.O + row + d0) = o;
-        }
+        const bf16x4 rb = residual(4 * b + q4, d0);
+        v[0] += (float)rb[0];
+        v[1] += (float)rb[1];
+        v[2] += (float)rb[2];
+        v[3] += (float)rb[3];
+        const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *(bf16x4*)(p.O + row + d0) = o;
       }
+  };
+  if (p.anchor) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = b * 32 + 8 * q4 + 4 * h;
+        const f32x4 r = *(const f32x4*)(p.Ofull + row + d0) - st.out4(b, q4, inv);
+        const bf16x4 rb = {(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+        *(bf16x4*)(p.R + row + d0) = rb;
+      }
+  } else if (!p.R) {
+    write_out([&](int, int) { return bf16x4{}; });
+  } else if (rlds && wu * 32 < RROWS) {
+    // this wave's residual rows sit in k0 (wave 0) or k1 (wave 1), row n, K-tile layout
+    const unsigned char* rrow = (wu == 0 ? k0 : k1) + n * (2 * D) + 8 * h;
+    write_out([&](int chunk, int) { return *(const bf16x4*)(rrow + 16 * (chunk ^ swz<D>(n))); });
+  } else {
+    write_out([&](int, int d0) { return *(const bf16x4*)(p.R + row + d0); });
   }
 }
 
@@ -197,11 +252,11 @@ void launch_ring(const Params& p, dim3 grid, int k, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_sparse_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
-                              hipStream_t st) {
+                              const int32_t* perm, const int32_t* idx, const float* Ofull, void* R, void* O,
+                              bool anchor, hipStream_t st) {
   Params p;
   p.Q = (const __bf16*)Q; p.K = (const __bf16*)K; p.V = (const __bf16*)V;
-  p.perm = perm; p.idx = idx; p.R = R; p.O = (__bf16*)O;
+  p.perm = perm; p.idx = idx; p.Ofull = Ofull; p.R = (__bf16*)R; p.O = (__bf16*)O;
   p.Nq = s.Nq; p.Nkv = s.Nkv; p.k = s.k; p.c = s.c;
   p.c_log2 = s.scale * kLog2e; p.causal_block = s.causal_block; p.q_offset = s.q_offset;
   p.anchor = anchor ? 1 : 0;

@@ -153,7 +153,7 @@ class MCSparseAttention:
         BH = p.B * p.H
         self.perm = torch.empty((p.B, p.H, p.Nq), dtype=torch.int32, device=device)
         self.idx = torch.empty((p.B, p.H, p.n_groups, p.k), dtype=torch.int32, device=device)
-        self.R = torch.empty((p.B, p.H, p.Nq, p.d), dtype=torch.float32, device=device)
+        self.R = torch.empty((p.B, p.H, p.Nq, p.d), dtype=dt, device=device)  # residual in the input dtype
         self.O = torch.empty((p.B, p.H, p.Nq, p.d), dtype=dt, device=device)
         g, _ = workspace_size(p, MCS_WS_GROUP)
         a, _ = workspace_size(p, MCS_WS_ANCHOR)

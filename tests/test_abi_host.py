@@ -107,6 +107,9 @@ def test_workspace_sizes():
     c = -(-1000 // 64)
     assert amin >= 4 * 2 * 1000 + 4 * c * 1200
     assert a >= amin + 4 * c * 1200
+    # bf16: the anchor also keeps the float32 dense output of every head (2 heads x 1000 x 128)
+    a32, amin32 = mcs.workspace_size(base(dtype="f32"), mcs.MCS_WS_ANCHOR)
+    assert amin - amin32 >= 4 * 2 * 1000 * 128 and a - a32 == amin - amin32
     with pytest.raises(mcs.MCSError) as e:
         mcs.workspace_size(p, 9)
     assert e.value.status == mcs.MCS_ERR_INVALID_ARG
