@@ -8,7 +8,10 @@ steps' drifted inputs.  All inputs are generated up front and resident in HBM
 before the timed region.  Every library call is bracketed by HIP events on
 the stream the library launches on; the metric is the reuse step
 (mcs_sparse_attn).  The library's own exact attention (mcs_dense_attn) is
-timed on the same rotating inputs as the comparator.
+timed on the same rotating inputs as the comparator.  Before every timed call
+a 512 MB scratch buffer (twice the 256 MB Infinity Cache) is overwritten, so
+headline times are cold-cache; warm-cache times (back-to-back calls on one
+step's inputs) are reported beside them.
 
 Prints one JSON line (rank 0).  See --help.
 """
@@ -40,6 +43,9 @@ def parse():
     ap.add_argument("--config", default="bidir5", help="workload name (synth.CONFIGS)")
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not overwrite the cache-flush buffer between calls")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm-cache reuse calls (profiler counter runs: every reuse launch is then cold)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for profiler counter calibration)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DB", "OUT_MD", "CMD"),
@@ -90,14 +96,21 @@ def _short_kernel(name: str) -> str:
 
 def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
     """Markdown table of per-kernel durations from a rocprofv3 kernel-trace
-    database (via rocpd2summary)."""
-    import csv
-    import subprocess
-    import tempfile
-    tmp = tempfile.mkdtemp()
-    subprocess.run(["rocpd2summary", "-i", os.path.abspath(db), "-f", "csv", "-d", tmp], check=True,
-                   capture_output=True, cwd=tmp)
-    rows = list(csv.DictReader(open(os.path.join(tmp, "kernels_summary.csv"))))
+    database (its `kernels` view, read with sqlite3).  Reuse-kernel launches
+    that directly follow a top-k launch are the anchor's epilogue (they form
+    R); they get a row of their own so that the reuse row is comparable with
+    the live timing of mcs_sparse_attn."""
+    import sqlite3
+    con = sqlite3.connect(os.path.abspath(db))
+    rows = con.execute("select name, start, end from kernels order by start").fetchall()
+    con.close()
+    stats, prev = {}, ""
+    for name, t0, t1 in rows:
+        k = _short_kernel(name)
+        key = k + " (anchor epilogue)" if k.startswith("sparse_ring_kernel") and prev.startswith("topk_kernel") else k
+        stats.setdefault(key, []).append((t1 - t0) / 1e3)
+        prev = k
+    total = sum(sum(v) for v in stats.values())
     with open(out, "w") as f:
         f.write(f"# {title}\n\nCommand (repository root, one MI355X; `cd /tmp && export TMPDIR=/tmp` for the "
                 f"profiler's scratch):\n\n```\n{cmd}\n```\n\n")
@@ -105,12 +118,9 @@ def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
             f.write(note + "\n\n")
         f.write("| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | % time |\n"
                 "|---|---:|---:|---:|---:|---:|---:|\n")
-        for r in rows:
-            name = r["Name"].replace("void ", "").replace("mcs::(anonymous namespace)::", "")
-            name = name.split("(mcs::")[0]
-            f.write(f"| `{name}` | {r['Calls']} | {float(r['Average (Nsec)']) / 1e3:.1f} | "
-                    f"{float(r['Min (Nsec)']) / 1e3:.1f} | {float(r['Max (Nsec)']) / 1e3:.1f} | "
-                    f"{float(r['Duration (Nsec)']) / 1e6:.2f} | {float(r['Percent (Inc)']):.1f} |\n")
+        for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+            f.write(f"| `{k}` | {len(v)} | {statistics.fmean(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                    f"{sum(v) / 1e3:.2f} | {100 * sum(v) / total:.1f} |\n")
     print(open(out).read())
 
 
@@ -172,6 +182,26 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(open(out).read())
+
+
+def device_max_sclk_mhz() -> float:
+    """Maximum engine clock of the first gfx950 agent, from rocminfo (run as
+    a child process); 0 when it cannot be read."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return 0.0
+    gpu = False
+    for line in out.splitlines():
+        if "gfx950" in line:
+            gpu = True
+        if gpu and "Max Clock Freq. (MHz)" in line:
+            try:
+                return float(line.split(":")[1].split()[0])
+            except (IndexError, ValueError):
+                return 0.0
+    return 0.0
 
 
 def reuse_bytes_per_launch(w) -> float:
@@ -275,9 +305,18 @@ def main():
     st = mcs.MCSparseAttention(p)
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    nflush = [0]
+
+    def flush():
+        # overwrite more than the Infinity Cache holds, outside every timed bracket
+        if not args.no_flush:
+            nflush[0] += 1
+            scratch.fill_(nflush[0] & 255)
 
     def period(record):
         e0, e1, e2 = ev(), ev(), ev()
+        flush()
         e0.record(stream)
         mcs.group(p, step_in[0][0], st.perm, st.ws_group, stream=stream)
         e1.record(stream)
@@ -286,6 +325,7 @@ def main():
         re = []
         for s in range(1, A):
             a, b = ev(), ev()
+            flush()
             a.record(stream)
             mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
             b.record(stream)
@@ -315,12 +355,43 @@ def main():
     for i in range(max(1, len(reuse_ms) // 2)):
         s = 1 + i % (A - 1)
         a, b = ev(), ev()
+        flush()
         a.record(stream)
         mcs.dense_attn(p, *step_in[s], Od, stream=stream)
         b.record(stream)
         dense_ms.append((a, b))
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dense_ms]
+
+    # warm cache: back-to-back calls on one step's inputs, no flush
+    warm = []
+    for i in range(0 if args.no_warm else 23):
+        a, b = ev(), ev()
+        a.record(stream)
+        mcs.sparse_attn(p, *step_in[1], st.perm, st.idx, st.R, st.O, stream=stream)
+        b.record(stream)
+        if i >= 3:
+            warm.append((a, b))
+    torch.cuda.synchronize()
+    warm_ms = [a.elapsed_time(b) for a, b in warm]
+
+    # HBM copy bandwidth measured on this device (1 GiB read + 1 GiB written per copy)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copies = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        copies.append((a, b))
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) / (statistics.median(a.elapsed_time(b) for a, b in copies) * 1e-3) / 1e9
+    del src, dst
+    props = torch.cuda.get_device_properties(0)
+    cus = int(getattr(props, "multi_processor_count", 0))
+    sclk_mhz = device_max_sclk_mhz()
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -366,6 +437,12 @@ def main():
         "dense_tflops": round(f_dense / (d_mean * 1e-3) / 1e12, 2),
         "dense_frac_bf16_peak": round(f_dense / (d_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "speedup_reuse_vs_dense": round(d_mean / r_mean, 2),
+        "cache": "flushed (512 MB overwrite before every timed call)" if not args.no_flush else "not flushed",
+        "reuse_ms_warm_median": round(statistics.median(warm_ms), 4) if warm else None,
+        "hbm_copy_gbs_measured": round(copy_gbs, 1),
+        "device_cus": cus,
+        "device_max_sclk_mhz": sclk_mhz,
+        "peak_bf16_tflops_from_device": round(cus * sclk_mhz * 1e6 * 4096 / 1e12, 1) if cus and sclk_mhz else None,
         "group_ms": round(statistics.fmean(group_ms), 4),
         "anchor_ms": round(statistics.fmean(anchor_ms), 4),
         "period_effective_tflops_dense_equiv": round(A * f_dense / (wall / args.steps) / 1e12, 2),

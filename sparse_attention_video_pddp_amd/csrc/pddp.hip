@@ -507,9 +507,14 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       for (int b = 0; b < NB; ++b) op[b] = cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
       if (valid < TR) {
         const __bf16 z = (__bf16)0.0f;
+        // rows of this lane relative to the tail, recomputed here (an opaque
+        // copy keeps the compiler from hoisting the comparisons out of the
+        // tile loop and spilling them)
+        int rel = valid - 16 * ks2 - 4 * h;
+        asm volatile("" : "+v"(rel));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool k0 = 16 * ks2 + 4 * h + j < valid, k1 = 16 * ks2 + 8 + 4 * h + j < valid;
+          const bool k0 = j < rel, k1 = 8 + j < rel;
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             op[b][j] = k0 ? op[b][j] : z;
