@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not overwrite the cache-flush buffer between calls")
+    ap.add_argument("--no-fidelity", action="store_true",
+                    help="skip the untimed fidelity diagnostic (reuse output against exact attention)")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm-cache reuse calls (profiler counter runs: every reuse launch is then cold)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -363,6 +365,26 @@ def main():
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dense_ms]
 
+    # fidelity diagnostic (untimed): relative error of the reuse output against the
+    # library's exact attention on the same step, with and without the residual, by
+    # steps since the anchor (the last timed period's anchor state is still in place)
+    fid_r, fid_nor, fid_stale = [], [], []
+    if not args.no_fidelity:
+        On = torch.empty_like(st.O)
+        O0 = torch.empty_like(st.O)
+        mcs.dense_attn(p, *step_in[0], O0, stream=stream)  # the anchor step's exact output
+        for s in range(1, A):
+            mcs.dense_attn(p, *step_in[s], Od, stream=stream)
+            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
+            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, None, On, stream=stream)
+            ref = Od.float()
+            nrm = ref.norm().item()
+            fid_r.append(round((st.O.float() - ref).norm().item() / nrm, 6))
+            fid_nor.append(round((On.float() - ref).norm().item() / nrm, 6))
+            fid_stale.append(round((O0.float() - ref).norm().item() / nrm, 6))
+        del On, O0
+        torch.cuda.synchronize()
+
     # warm cache: back-to-back calls on one step's inputs, no flush
     warm = []
     for i in range(0 if args.no_warm else 23):
@@ -438,6 +460,9 @@ def main():
         "dense_frac_bf16_peak": round(f_dense / (d_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "speedup_reuse_vs_dense": round(d_mean / r_mean, 2),
         "cache": "flushed (512 MB overwrite before every timed call)" if not args.no_flush else "not flushed",
+        "fidelity_rel_err_with_R": fid_r or None,
+        "fidelity_rel_err_without_R": fid_nor or None,
+        "fidelity_rel_err_stale_anchor_output": fid_stale or None,
         "reuse_ms_warm_median": round(statistics.median(warm_ms), 4) if warm else None,
         "hbm_copy_gbs_measured": round(copy_gbs, 1),
         "device_cus": cus,
