@@ -26,6 +26,10 @@ SMALL = {
     "large_small": synth.get("large").with_(name="large_small", H=2, grid=(4, 15, 20), keep_permille=300),
     # 3D-local field generator, d=64, G=128: 2048 tokens -> 16 groups, k=205
     "stress_small": synth.get("stress").with_(name="stress_small", H=2, grid=(8, 16, 16), keep_permille=100),
+    # batch of two videos (B=2, H=2): every (b, h) has its own grouping, selection and residual
+    "batch_small": synth.get("bidir5").with_(name="batch_small", B=2, H=2, grid=(2, 12, 20), keep_permille=150),
+    # fp32 path with B=2
+    "tiny_batch": synth.get("tiny").with_(name="tiny_batch", B=2, H=1, grid=(2, 16, 16)),
 }
 
 
@@ -40,7 +44,7 @@ def cuda():
 def test_small_workload_parity(cuda, name):
     from tests.gpu_runner import log, run_anchor_reuse
     w = SMALL[name]
-    heads = [(0, h) for h in range(w.H)]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     cases = run_anchor_reuse(w, heads)
     for bh, case in cases.items():
         reps = check_head(case, w.group_size, w.k, w.scale, w.causal_block, w.q_offset, w.pddp_iters)
