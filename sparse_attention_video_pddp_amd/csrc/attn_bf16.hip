@@ -202,6 +202,7 @@ __device__ __forceinline__ int visible_limit(int qpos, int causal_block, int q_o
 
 // ---------------------------------------------------------------------------
 // Dense attention: 128 queries (4 waves) per workgroup, natural token order.
+// Two waves per SIMD at d = 128 (250 registers), three at d = 64.
 // ---------------------------------------------------------------------------
 struct DenseParams {
   const __bf16 *Q, *K, *V;
@@ -214,7 +215,7 @@ struct DenseParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dense_bf16_kernel(DenseParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2))) void dense_bf16_kernel(DenseParams p) {
   constexpr int NT = 256, QR = 128;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * Tile<D>::KS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[64 * Tile<D>::VS];
@@ -258,9 +259,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ---------------------------------------------------------------------------
 // Anchor column mass: m_g[j] = sum_{i in g} exp(scale*<q_i,k_j> - lse_i).
-// 128 queries (4 waves) per workgroup = 128/G groups.  Scores are formed as
-// S = Q K^T here so that a lane holds one key column: its mass over the
-// wave's 32 queries is in-lane plus one half-wave exchange.
+// Scores are formed as S = Q K^T here so that a lane holds one key column.
+// Each wave owns 64 queries as two 32-row MFMA blocks that share every K
+// operand read from LDS (half the LDS traffic per MFMA of a 32-query wave);
+// a lane's mass over the wave's 64 queries is in-lane plus one half-wave
+// exchange.  A 64-query group is one wave and its sums go straight to
+// memory; a 128-query group is two waves whose sums meet in LDS.
 // ---------------------------------------------------------------------------
 struct MassParams {
   const __bf16 *Q, *K;
@@ -270,129 +274,164 @@ struct MassParams {
   int Nq, Nkv, c, bh0, upb, n_units, per_xcd;
   float c_log2;
   int causal_block, q_offset;
+  int nsplit, tps;  // key ranges per query block, 64-key tiles per range
 };
 
-template <int D>
+template <int D, int NW>
 struct MassTile {
-  static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int RPL = 64 / CH;       // rows per wave-wide copy
-  static constexpr int LPW = 64 / RPL / 4;  // copies per wave per 64-key tile
+  static constexpr int CH = D / 8;           // 16-byte chunks per row
+  static constexpr int RPL = 64 / CH;        // rows per wave-wide copy
+  static constexpr int LPW = 64 / RPL / NW;  // copies per wave per 64-key tile
   static constexpr int BYTES = 64 * D * 2;
 };
 
-// K tiles of 64 keys arrive by direct-to-LDS copies in a two-slot ring (row
-// layout and swizzle of ring.hpp); one barrier per tile, which also orders the
-// per-wave column sums of the previous tile (double-buffered) before their
-// reduction over the group's waves.  A tile that every query of the wave sees
-// in full takes the unmasked path.  Three waves per SIMD: within 168
-// registers the scores stay in VGPRs (no accumulator-register copies, which
-// would cost VALU issue slots).
-template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void mass_bf16_kernel(MassParams p) {
-  using T = MassTile<D>;
-  constexpr int QR = 128, GPW = QR / G, WPG = G / 32, NKS = D / 16;
+// NW waves (64 * NW queries) per workgroup over one range of tps K tiles
+// (the mass of a key depends on no other key, so workloads with few query
+// blocks split the keys to fill the chip).  K tiles of 64 keys arrive by
+// direct-to-LDS copies in a two-slot ring (row layout and swizzle of
+// ring.hpp), one barrier per tile; for two-wave groups that barrier also
+// orders the per-wave sums of the previous tile (double-buffered) before they
+// are added.  Per-query lse and visibility limits are staged in LDS: the lse
+// values are read once into registers, the limits only by tiles that some
+// query of the wave sees in part.  Three waves per SIMD at d = 128 (within
+// 168 registers), four at d = 64: the exponentials and the per-score VALU
+// work of one wave run beside the MFMAs of the others.
+template <int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3))) void mass_bf16_kernel(MassParams p) {
+  using T = MassTile<D, NW>;
+  constexpr int QR = 64 * NW, WPG = G / 64, GPW = QR / G, NKS = D / 16;
+  static_assert(WPG == 1 || WPG == 2, "group size");
+  static_assert(T::LPW >= 1, "copies per wave");
   __shared__ __attribute__((aligned(1024))) unsigned char k0[T::BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char k1[T::BYTES];
-  __shared__ float part[2][4][64];
-  __shared__ int s_kmax[4];
+  __shared__ float part[WPG > 1 ? 2 : 1][NW][64];
+  __shared__ __attribute__((aligned(16))) float s_lse[NW][64];
+  __shared__ __attribute__((aligned(16))) int s_lim[NW][64];
+  __shared__ int s_kmax[NW];
   const int unit = xcd_unit(blockIdx.x, p.per_xcd);
   if (unit >= p.n_units) return;
-  const int bhl = unit / p.upb, u = unit - bhl * p.upb;
+  const int qunit = unit / p.nsplit, ksp = unit - qunit * p.nsplit;
+  const int bhl = qunit / p.upb, u = qunit - bhl * p.upb;
   const int bh = p.bh0 + bhl;
   const int w = wave_id(), l = lane_id(), n = l & 31, h = l >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int pos0 = u * QR + w * 32;
+  const int pos0 = u * QR + w * 64;
   const int32_t* hperm = p.perm + (size_t)bh * p.Nq;
-  const float* hlse = p.lse + (size_t)bh * p.Nq;
-  bf16x8 qa[NKS];
+  // query pos0 + l: its row, lse (base 2; padding rows +inf so they add 0) and limit
+  int lmax, lmin;
   {
-    const bool v = pos0 + n < p.Nq;
-    const int row = v ? min(max(hperm[pos0 + n], 0), p.Nq - 1) : 0;
-    const __bf16* qp = p.Q + ((size_t)bh * p.Nq + row) * D + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 z = {};
-      qa[ks] = v ? *(const bf16x8*)(qp + ks * 16) : z;
-    }
-  }
-  // per score row i of this lane: query 8*(i/4) + 4*h + i%4 of the wave
-  float lse2[16];
-  int lim[16];
-  int lmax = 0, lmin = p.Nkv;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int qp = pos0 + 8 * (i >> 2) + 4 * h + (i & 3);
-    if (qp < p.Nq) {
-      const int row = min(max(hperm[qp], 0), p.Nq - 1);
-      const float ls = hlse[row];
-      lse2[i] = (ls == -kInf) ? kInf : ls * kLog2e;
-      lim[i] = visible_limit(row, p.causal_block, p.q_offset, p.Nkv);
-      lmin = min(lmin, lim[i]);
-    } else {
-      lse2[i] = kInf;  // exp2(-inf) = 0: padding rows add nothing
-      lim[i] = 0;
-    }
-    lmax = max(lmax, lim[i]);
+    const bool v = pos0 + l < p.Nq;
+    const int row = v ? min(max(hperm[pos0 + l], 0), p.Nq - 1) : 0;
+    const float ls = p.lse[(size_t)bh * p.Nq + row];
+    s_lse[w][l] = (!v || ls == -kInf) ? kInf : ls * kLog2e;
+    const int lim = v ? visible_limit(row, p.causal_block, p.q_offset, p.Nkv) : 0;
+    s_lim[w][l] = lim;
+    lmax = lim;
+    lmin = v ? lim : p.Nkv;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     lmax = max(lmax, __shfl_xor(lmax, o, 64));
     lmin = min(lmin, __shfl_xor(lmin, o, 64));
   }
+  bf16x8 qa[2][NKS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const bool v = pos0 + 32 * qb + n < p.Nq;
+    const int row = v ? min(max(hperm[pos0 + 32 * qb + n], 0), p.Nq - 1) : 0;
+    const __bf16* qp = p.Q + ((size_t)bh * p.Nq + row) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 z = {};
+      qa[qb][ks] = v ? *(const bf16x8*)(qp + ks * 16) : z;
+    }
+  }
   if (l == 0) s_kmax[w] = lmax;
   __syncthreads();
-  const int kmax = max(max(s_kmax[0], s_kmax[1]), max(s_kmax[2], s_kmax[3]));
-  const int ntiles = (kmax + 63) / 64;
+  int kmax = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) kmax = max(kmax, s_kmax[i]);
+  const int t0 = ksp * p.tps;
+  const int ntiles = max(0, min((kmax + 63) / 64, t0 + p.tps) - t0);  // tiles t0 .. t0 + ntiles - 1
+  // score row i of block qb on this lane: query 32*qb + 8*(i/4) + 4*h + i%4 of the wave
+  float lse2[2][16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 v4 = *(const f32x4*)&s_lse[w][32 * qb + 8 * r + 4 * h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lse2[qb][4 * r + e] = v4[e];
+    }
   const __bf16* Kh = p.K + (size_t)bh * p.Nkv * D;
   const int kbase = n * (2 * D) + 16 * (h ^ swz<D>(n));
   int voff[T::LPW];
 #pragma unroll
   for (int j = 0; j < T::LPW; ++j) {
-    const int r = T::RPL * (wu + 4 * j) + l / T::CH;
+    const int r = T::RPL * (wu + NW * j) + l / T::CH;
     voff[j] = r * (2 * D) + (((l % T::CH) ^ swz<D>(r)) * 16);
   }
   // rows past the end of the head read as zeros (their keys are masked)
-  auto issue = [&](int t, unsigned char* slot) {
+  auto issue = [&](int i, unsigned char* slot) {
+    const int t = t0 + i;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(Kh + (size_t)t * 64 * D, (p.Nkv - t * 64) * D * 2);
 #pragma unroll
-    for (int j = 0; j < T::LPW; ++j) dma16_buf(r, voff[j], slot + (wu + 4 * j) * 1024);
+    for (int j = 0; j < T::LPW; ++j) dma16_buf(r, voff[j], slot + (wu + NW * j) * 1024);
   };
-  // group sums of the tile whose per-wave sums are in part[b]
-  auto reduce = [&](int t, int b) {
-    if (threadIdx.x < GPW * 64) {
-      const int gl = threadIdx.x >> 6, key = threadIdx.x & 63;
-      float m = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < WPG; ++ww) m += part[b][gl * WPG + ww][key];
-      const int gg = u * GPW + gl;
-      if (gg < p.c && t * 64 + key < p.Nkv) p.mass[((size_t)bhl * p.c + gg) * p.Nkv + t * 64 + key] = m;
+  // group sums of tile t0 + i, whose per-wave sums are in part[b] (two-wave groups)
+  auto reduce = [&](int i, int b) {
+    if constexpr (WPG > 1) {
+      const int t = t0 + i;
+      if (threadIdx.x < GPW * 64) {
+        const int gl = threadIdx.x >> 6, key = threadIdx.x & 63;
+        const float m = part[b][2 * gl][key] + part[b][2 * gl + 1][key];
+        const int gg = u * GPW + gl;
+        if (gg < p.c && t * 64 + key < p.Nkv) p.mass[((size_t)bhl * p.c + gg) * p.Nkv + t * 64 + key] = m;
+      }
     }
   };
-  auto tile = [&](int t, const unsigned char* Ks, int b) {
-    const int base = t * 64;
+  auto tile = [&](int i, const unsigned char* Ks, int b) {
+    const int base = (t0 + i) * 64;
     const bool full = base + 64 <= lmin;  // every key of the tile visible to every query of the wave
+    float cs2[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = {};
+      f32x16 s[2] = {};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 kk = *(const bf16x8*)(Ks + kb * 32 * 2 * D + (kbase ^ (32 * ks)));
-        s = mfma_32x32x16(qa[ks], kk, s);
+        s[0] = mfma_32x32x16(qa[0][ks], kk, s[0]);
+        s[1] = mfma_32x32x16(qa[1][ks], kk, s[1]);
       }
       float cs = 0.f;
       if (full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) cs += fast_exp2(fmaf(s[i], p.c_log2, -lse2[i]));
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) cs += fast_exp2(fmaf(s[qb][i], p.c_log2, -lse2[qb][i]));
       } else {
         const int key = base + kb * 32 + n;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(fmaf(s[i], p.c_log2, -lse2[i]));
-          cs += (key < lim[i]) ? pv : 0.f;
-        }
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int4 lm = *(const int4*)&s_lim[w][32 * qb + 8 * r + 4 * h];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = fast_exp2(fmaf(s[qb][4 * r + e], p.c_log2, -lse2[qb][4 * r + e]));
+              cs += (key < lm[e]) ? pv : 0.f;
+            }
+          }
       }
-      cs = half_sum(cs);
-      if (h == 0) part[b][w][kb * 32 + n] = cs;
+      cs2[kb] = half_sum(cs);
+    }
+    // lane (h, n) holds key 32*h + n of the tile
+    const float out = h ? cs2[1] : cs2[0];
+    if constexpr (WPG == 1) {
+      const int gg = u * GPW + w, key = base + 32 * h + n;
+      if (gg < p.c && key < p.Nkv) p.mass[((size_t)bhl * p.c + gg) * p.Nkv + key] = out;
+    } else {
+      part[b][w][l] = out;
     }
   };
   if (ntiles > 0) {
@@ -415,8 +454,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     __syncthreads();
     if (t + 3 < ntiles) issue(t + 3, k1);
   }
-  __syncthreads();
-  if (ntiles > 0) reduce(ntiles - 1, (ntiles - 1) & 1);
+  if constexpr (WPG > 1) {
+    __syncthreads();
+    if (ntiles > 0) reduce(ntiles - 1, (ntiles - 1) & 1);
+  }
 }
 
 template <typename P>
@@ -447,15 +488,24 @@ hipError_t launch_mass_bf16(const Shape& s, int bh0, int nbh, const void* Q, con
   MassParams p;
   p.Q = (const __bf16*)Q; p.K = (const __bf16*)K; p.perm = perm; p.lse = lse; p.mass = mass;
   p.Nq = s.Nq; p.Nkv = s.Nkv; p.c = s.c; p.bh0 = bh0;
-  const int gpw = 128 / s.G;
-  p.upb = (s.c + gpw - 1) / gpw;
   p.c_log2 = s.scale * kLog2e; p.causal_block = s.causal_block; p.q_offset = s.q_offset;
+  // four-wave workgroups (one K tile serves 256 queries); the keys are split
+  // into ranges when the query blocks alone give fewer than ~6 waves per SIMD
+  constexpr int kQR = 256, kWaveTarget = 6144;
+  p.upb = (s.Nq + kQR - 1) / kQR;
+  const int kt = (s.Nkv + 63) / 64;
+  const long long waves = (long long)nbh * p.upb * (kQR / 64);
+  int ns = (int)std::min<long long>((kWaveTarget + waves - 1) / waves, std::max(1, kt / 4));
+  p.tps = (kt + ns - 1) / ns;
+  p.nsplit = (kt + p.tps - 1) / p.tps;
   dim3 grid;
-  grid_for(p, nbh * p.upb, grid);
-  if (s.d == 128 && s.G == 64) hipLaunchKernelGGL((mass_bf16_kernel<128, 64>), grid, dim3(256), 0, st, p);
-  else if (s.d == 128) hipLaunchKernelGGL((mass_bf16_kernel<128, 128>), grid, dim3(256), 0, st, p);
-  else if (s.G == 64) hipLaunchKernelGGL((mass_bf16_kernel<64, 64>), grid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((mass_bf16_kernel<64, 128>), grid, dim3(256), 0, st, p);
+  grid_for(p, nbh * p.upb * p.nsplit, grid);
+#define MCS_MASS(DD, GG) hipLaunchKernelGGL((mass_bf16_kernel<DD, GG, 4>), grid, dim3(256), 0, st, p)
+  if (s.d == 128 && s.G == 64) MCS_MASS(128, 64);
+  else if (s.d == 128) MCS_MASS(128, 128);
+  else if (s.G == 64) MCS_MASS(64, 64);
+  else MCS_MASS(64, 128);
+#undef MCS_MASS
   return hipGetLastError();
 }
 
