@@ -235,6 +235,62 @@ def topk_select(mass: np.ndarray, k: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Block-sparse comparator: mean-pooled block selection
+# ---------------------------------------------------------------------------
+def block_pooled_selection(Q, K, G: int, k: int, scale: float, causal_block: int = 0,
+                           q_offset: int = 0, block: int = 64,
+                           groups: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Selection of block-sparse attention with mean-pooled scoring, the
+    approach MC-Sparse is measured against (review page, section 1 on
+    selection error from approximate scoring such as mean pooling and on
+    structural binding error; section 2 on block-granular sparsity).
+
+    Readings (the page gives no formulas): query blocks are the G-token tiles
+    of the token order and KV blocks the ``block``-token tiles (each last
+    tile may be short); a block is represented by the mean of its rows, and
+    the score of KV block b for query block g is scale*<mean q_g, mean k_b>.
+    KV blocks none of whose keys is visible to any query of g rank after
+    every other block.  Blocks are taken in order of decreasing score (ties to
+    the lower block index) while the token count stays within k; the next
+    block then contributes its lowest-index tokens up to exactly k.  Returns
+    [c, k] token indices, ascending per row (rows of groups not listed in
+    ``groups`` stay -1).
+    """
+    Q, K = _as64(Q), _as64(K)
+    Nq, Nkv = Q.shape[0], K.shape[0]
+    nkb = -(-Nkv // block)
+    kb = [np.arange(b * block, min((b + 1) * block, Nkv)) for b in range(nkb)]
+    kbar = np.stack([K[keys].mean(axis=0) for keys in kb])
+    sl = group_slices(Nq, G)
+    out = np.full((len(sl), k), -1, dtype=np.int64)
+    for g in (range(len(sl)) if groups is None else groups):
+        rows = np.arange(sl[g].start, sl[g].stop)
+        score = scale * (kbar @ Q[rows].mean(axis=0))
+        cand = np.array([visible(rows, keys, causal_block, q_offset).any() for keys in kb])
+        score = np.where(cand, score, -np.inf)
+        order = np.lexsort((np.arange(nkb), -score))   # score descending, block index ascending
+        sel: List[int] = []
+        for b in order:
+            sel.extend(kb[b][:k - len(sel)].tolist())
+            if len(sel) == k:
+                break
+        out[g] = np.sort(np.asarray(sel, dtype=np.int64))
+    return out
+
+
+def block_sparse_step(Q, K, V, G: int, k: int, scale: float, causal_block: int = 0,
+                      q_offset: int = 0, groups: Optional[Sequence[int]] = None):
+    """One step of the block-sparse comparator: the mean-pooled selection of
+    this step's Q/K, then attention of each query block over its selected
+    tokens (no residual).  Query blocks are token-order tiles, so the grouping
+    is the identity.  Returns (perm, idx, O)."""
+    perm = np.arange(_as64(Q).shape[0], dtype=np.int64)
+    idx = block_pooled_selection(Q, K, G, k, scale, causal_block, q_offset, groups=groups)
+    O = sparse_attention(Q, K, V, perm, idx, G, scale, causal_block, q_offset, groups)
+    return perm, idx, O
+
+
+# ---------------------------------------------------------------------------
 # Gathered sparse attention, residual and reuse
 # ---------------------------------------------------------------------------
 def sparse_attention(Q, K, V, perm: np.ndarray, idx: np.ndarray, G: int, scale: float,
