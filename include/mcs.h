@@ -54,7 +54,11 @@ typedef enum mcs_status {
 
 typedef enum mcs_dtype { MCS_F32 = 0, MCS_BF16 = 1 } mcs_dtype;
 
-typedef enum mcs_workspace_kind { MCS_WS_GROUP = 0, MCS_WS_ANCHOR = 1 } mcs_workspace_kind;
+typedef enum mcs_workspace_kind {
+  MCS_WS_GROUP = 0,
+  MCS_WS_ANCHOR = 1,
+  MCS_WS_BLOCK = 2
+} mcs_workspace_kind;
 
 /* Problem description.  Supported: d in {64,128}; group_size in {64,128};
  * 1 <= k <= Nkv, and k <= 28672 for bf16 (a group's kept-key list is held
@@ -75,8 +79,9 @@ typedef struct mcs_problem {
   int32_t dtype;        /* mcs_dtype of Q, K, V, O                             */
 } mcs_problem;
 
-/* Bytes of workspace mcs_group (kind MCS_WS_GROUP) or mcs_anchor
- * (MCS_WS_ANCHOR) needs to process all B*H heads in one pass.  For
+/* Bytes of workspace mcs_group (kind MCS_WS_GROUP), mcs_anchor
+ * (MCS_WS_ANCHOR) or mcs_block_select (MCS_WS_BLOCK) needs to process all B*H
+ * heads in one pass.  For
  * MCS_WS_ANCHOR any size of at least `*min_bytes` works (heads are then
  * processed in chunks); min_bytes may be NULL.  For bf16 problems the anchor
  * workspace also holds the float32 O_full of all heads (B*H*Nq*d*4 bytes, part
@@ -139,6 +144,26 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,
                            const int32_t* perm, const int32_t* idx, const void* R, void* O,
                            void* stream);
+
+/* Selection of the block-sparse comparator, recomputed on every step
+ * (MC-Sparse review, section 1: selection error of approximate scoring such as
+ * mean pooling, structural binding error of whole-block selection; section 2:
+ * block-sparse attention).  Query blocks are the G-token tiles of the token
+ * order and KV blocks the 64-token tiles (each last tile may be short).  With
+ * mean pooled block vectors, KV block b scores scale*<mean q_g, mean k_b> for
+ * query block g; blocks with no key visible to any query of g rank last.
+ * Blocks are taken by decreasing score (ties to the lower block index) while
+ * the token count stays within k, and the next block gives its lowest-index
+ * tokens up to exactly k.  The outputs have the shapes mcs_anchor gives, so
+ * mcs_sparse_attn(perm, idx, R = NULL) then runs the block-sparse attention.
+ *   perm [B,H,Nq] int32, written with the identity (query blocks are tiles).
+ *   idx  [B,H,c,k] int32, written: each query block's selected tokens, ascending.
+ *   ws   workspace of at least mcs_workspace_size(MCS_WS_BLOCK) bytes
+ *        (float32 pooled vectors of every tile).
+ * Unsupported (MCS_ERR_UNSUPPORTED): more than 8192 KV blocks (Nkv > 524288)
+ * or k > 32705 (more than 512 blocks to rank). */
+mcs_status mcs_block_select(const mcs_problem* p, const void* Q, const void* K, int32_t* perm, int32_t* idx,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* mcs_status_string(mcs_status s);

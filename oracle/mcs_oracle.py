@@ -237,6 +237,24 @@ def topk_select(mass: np.ndarray, k: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Block-sparse comparator: mean-pooled block selection
 # ---------------------------------------------------------------------------
+def block_scores(Q, K, rows: slice, scale: float, causal_block: int = 0, q_offset: int = 0,
+                 block: int = 64) -> np.ndarray:
+    """Mean-pooled score of every KV block for the query block ``rows``:
+    scale*<mean of the query rows, mean of the block's key rows>, or -inf for
+    a KV block none of whose keys is visible to any of the queries (see
+    block_pooled_selection)."""
+    Q, K = _as64(Q), _as64(K)
+    Nkv = K.shape[0]
+    qrows = np.arange(rows.start, rows.stop)
+    qbar = Q[qrows].mean(axis=0)
+    out = np.empty(-(-Nkv // block))
+    for b in range(out.size):
+        keys = np.arange(b * block, min((b + 1) * block, Nkv))
+        seen = visible(qrows, keys, causal_block, q_offset).any()
+        out[b] = scale * float(K[keys].mean(axis=0) @ qbar) if seen else -np.inf
+    return out
+
+
 def block_pooled_selection(Q, K, G: int, k: int, scale: float, causal_block: int = 0,
                            q_offset: int = 0, block: int = 64,
                            groups: Optional[Sequence[int]] = None) -> np.ndarray:
@@ -260,14 +278,10 @@ def block_pooled_selection(Q, K, G: int, k: int, scale: float, causal_block: int
     Nq, Nkv = Q.shape[0], K.shape[0]
     nkb = -(-Nkv // block)
     kb = [np.arange(b * block, min((b + 1) * block, Nkv)) for b in range(nkb)]
-    kbar = np.stack([K[keys].mean(axis=0) for keys in kb])
     sl = group_slices(Nq, G)
     out = np.full((len(sl), k), -1, dtype=np.int64)
     for g in (range(len(sl)) if groups is None else groups):
-        rows = np.arange(sl[g].start, sl[g].stop)
-        score = scale * (kbar @ Q[rows].mean(axis=0))
-        cand = np.array([visible(rows, keys, causal_block, q_offset).any() for keys in kb])
-        score = np.where(cand, score, -np.inf)
+        score = block_scores(Q, K, sl[g], scale, causal_block, q_offset, block)
         order = np.lexsort((np.arange(nkb), -score))   # score descending, block index ascending
         sel: List[int] = []
         for b in order:

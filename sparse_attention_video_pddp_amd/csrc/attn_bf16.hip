@@ -194,12 +194,6 @@ __device__ __forceinline__ void store_row_f32(float* dst, const Flash<D>& st, fl
     }
 }
 
-__device__ __forceinline__ int visible_limit(int qpos, int causal_block, int q_offset, int Nkv) {
-  if (!causal_block) return Nkv;
-  const long long lim = ((long long)(q_offset + qpos) / causal_block + 1) * causal_block;
-  return lim < Nkv ? (int)lim : Nkv;
-}
-
 // ---------------------------------------------------------------------------
 // Dense attention: 128 queries (4 waves) per workgroup, natural token order.
 // Two waves per SIMD at d = 128 (250 registers), three at d = 64.

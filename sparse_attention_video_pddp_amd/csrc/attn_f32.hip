@@ -22,12 +22,6 @@ struct F32Params {
   int causal_block, q_offset, anchor;
 };
 
-__device__ __forceinline__ int vis_limit(int qpos, int causal_block, int q_offset, int Nkv) {
-  if (!causal_block) return Nkv;
-  const long long lim = ((long long)(q_offset + qpos) / causal_block + 1) * causal_block;
-  return lim < Nkv ? (int)lim : Nkv;
-}
-
 // Online softmax over a list of keys for one query row held in registers.
 template <int D, typename KeyAt>
 __device__ __forceinline__ void attend_row(const float* q, const float* Kh, const float* Vh, int nkeys,
@@ -69,7 +63,7 @@ __global__ __launch_bounds__(64) void dense_f32_kernel(F32Params p) {
 #pragma unroll
   for (int i = 0; i < D; ++i) qv[i] = qp[i];
   double m, l;
-  const int nk = vis_limit(q, p.causal_block, p.q_offset, p.Nkv);
+  const int nk = visible_limit(q, p.causal_block, p.q_offset, p.Nkv);
   attend_row<D>(qv, p.K + (size_t)bh * p.Nkv * D, p.V + (size_t)bh * p.Nkv * D, nk,
                 [](int t) { return t; }, p.scale, o, m, l);
   const float inv = l > 0.0 ? (float)(1.0 / l) : 0.f;
@@ -92,7 +86,7 @@ __global__ __launch_bounds__(128) void sparse_f32_kernel(F32Params p) {
   const int32_t* sel = p.idx + ((size_t)bh * p.c + g) * p.k;
   int nk = p.k;
   if (p.causal_block) {
-    const int lim = vis_limit(q, p.causal_block, p.q_offset, p.Nkv);
+    const int lim = visible_limit(q, p.causal_block, p.q_offset, p.Nkv);
     int lo = 0, hi = p.k;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -132,7 +126,7 @@ __global__ __launch_bounds__(256) void mass_f32_kernel(F32Params p) {
     sq[e] = p.Q[((size_t)bh * p.Nq + q) * D + i];
     if (i == 0) {
       slse[r] = (double)p.lse_in[(size_t)bh * p.Nq + q];
-      slim[r] = vis_limit(q, p.causal_block, p.q_offset, p.Nkv);
+      slim[r] = visible_limit(q, p.causal_block, p.q_offset, p.Nkv);
     }
   }
   __syncthreads();

@@ -158,6 +158,8 @@ mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes,
       need = fixed + (size_t)c.s.BH * anchor_mass_bytes_per_head(c.s);
       need_min = fixed + anchor_mass_bytes_per_head(c.s);
     }
+  } else if (kind == MCS_WS_BLOCK) {
+    need = need_min = c.empty ? 0 : mcs::block_workspace_bytes(c.s);
   } else {
     return fail(MCS_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
   }
@@ -228,6 +230,25 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
   e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, ofull, R, nullptr, true, st)
              : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, (float*)R, nullptr, true, st);
   return hip_status(e, "mcs_anchor (sparse)");
+}
+
+mcs_status mcs_block_select(const mcs_problem* p, const void* Q, const void* K, int32_t* perm, int32_t* idx,
+                            void* ws, size_t ws_bytes, void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  const int nkb = (p->Nkv + mcs::kPoolBlock - 1) / mcs::kPoolBlock;
+  if (nkb > mcs::kMaxKvBlocks)
+    return fail(MCS_ERR_UNSUPPORTED, "Nkv=%d: %d KV blocks exceed %d", p->Nkv, nkb, mcs::kMaxKvBlocks);
+  if (mcs::block_select_count(p->k, nkb) > mcs::kMaxSelBlocks)
+    return fail(MCS_ERR_UNSUPPORTED, "k=%d needs more than %d ranked blocks", p->k, mcs::kMaxSelBlocks);
+  if (c.empty) return ok();
+  const size_t need = mcs::block_workspace_bytes(c.s);
+  if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "block workspace %zu < %zu bytes", ws_bytes, need);
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {perm, "perm", false}, {idx, "idx", false},
+                                 {ws, "ws", false}}))
+    return s;
+  return hip_status(mcs::launch_block_select(c.s, c.bf16, Q, K, perm, idx, ws, (hipStream_t)stream),
+                    "mcs_block_select");
 }
 
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,

@@ -66,6 +66,15 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Keys [0, limit) are visible to the query at position q_offset + qpos:
+// everything without a causal block, else every key up to the end of the
+// query's frame block (clamped to Nkv).  Nondecreasing in qpos.
+__device__ __forceinline__ int visible_limit(int qpos, int causal_block, int q_offset, int Nkv) {
+  if (!causal_block) return Nkv;
+  const long long lim = ((long long)(q_offset + qpos) / causal_block + 1) * causal_block;
+  return lim < Nkv ? (int)lim : Nkv;
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs in launch order.  Give each
 // XCD a contiguous range of logical work units so that units sharing K/V
 // (neighbouring query tiles or groups of one head) share that XCD's L2.

@@ -45,6 +45,24 @@ hipError_t launch_sparse_f32(const Shape& s, const void* Q, const void* K, const
                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
                              hipStream_t st);
 
+// Block-sparse comparator (mean-pooled block selection).  KV blocks of
+// kPoolBlock tokens; the scores of one query block's KV blocks are held in
+// LDS (at most kMaxKvBlocks) and the top J of them are ranked exactly (at
+// most kMaxSelBlocks).
+constexpr int kPoolBlock = 64;
+constexpr int kMaxKvBlocks = 8192;
+constexpr int kMaxSelBlocks = 512;
+// Blocks that certainly hold k tokens: J-1 full blocks and at least one more
+// token (every block but the last has kPoolBlock tokens).
+inline __host__ __device__ int block_select_count(int k, int nkb) {
+  const int j = (k - 1 + kPoolBlock - 1) / kPoolBlock + 1;
+  return j < nkb ? j : nkb;
+}
+// ws: float32 pooled queries [BH*c*d] then pooled keys [BH*nkb*d].
+size_t block_workspace_bytes(const Shape& s);
+hipError_t launch_block_select(const Shape& s, bool bf16, const void* Q, const void* K, int32_t* perm,
+                               int32_t* idx, void* ws, hipStream_t st);
+
 // PDDP grouping.  ws: int32 tmp [BH*Nq] followed by uint32 keys [BH*Nq].
 size_t pddp_workspace_bytes(const Shape& s);
 hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, void* ws, hipStream_t st);

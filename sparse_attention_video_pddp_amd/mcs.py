@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_PKG, "libmcs.so")
 
 MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
 MCS_F32, MCS_BF16 = 0, 1
-MCS_WS_GROUP, MCS_WS_ANCHOR = 0, 1
+MCS_WS_GROUP, MCS_WS_ANCHOR, MCS_WS_BLOCK = 0, 1, 2
 
 EXPORTED = ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
-            "mcs_status_string", "mcs_last_error", "mcs_version")
+            "mcs_block_select", "mcs_status_string", "mcs_last_error", "mcs_version")
 
 
 class Problem(ctypes.Structure):
@@ -68,7 +68,9 @@ def lib() -> ctypes.CDLL:
         L.mcs_dense_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
         L.mcs_anchor.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mcs_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-        for f in ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn"):
+        L.mcs_block_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        for f in ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
+                  "mcs_block_select"):
             getattr(L, f).restype = ctypes.c_int
         L.mcs_status_string.argtypes = [ctypes.c_int]
         L.mcs_status_string.restype = ctypes.c_char_p
@@ -140,6 +142,12 @@ def sparse_attn(p: Problem, Q, K, V, perm, idx, R, O, stream=None) -> None:
                                  _ptr(O), _stream(stream)))
 
 
+def block_select(p: Problem, Q, K, perm, idx, ws, ws_bytes: Optional[int] = None, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().mcs_block_select(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(perm), _ptr(idx), _ptr(ws), nbytes,
+                                  _stream(stream)))
+
+
 class MCSparseAttention:
     """Per-layer state of the method across denoising steps: the groups
     (perm), selections (idx) and residual (R) of the last anchor, held in
@@ -170,4 +178,25 @@ class MCSparseAttention:
             if not self.has_anchor:
                 raise RuntimeError("a reuse step needs a previous anchor step")
             sparse_attn(self.p, Q, K, V, self.perm, self.idx, self.R, self.O, stream=stream)
+        return self.O
+
+
+class BlockSparseComparator:
+    """The block-sparse comparator at the same token budget k: the mean-pooled
+    block selection recomputed from every step's Q/K, then attention over the
+    selected tokens with no residual.  ``step(Q, K, V)`` returns O."""
+
+    def __init__(self, p: Problem, device="cuda"):
+        import torch
+        self.p = p
+        dt = torch.bfloat16 if p.dtype == MCS_BF16 else torch.float32
+        self.perm = torch.empty((p.B, p.H, p.Nq), dtype=torch.int32, device=device)
+        self.idx = torch.empty((p.B, p.H, p.n_groups, p.k), dtype=torch.int32, device=device)
+        self.O = torch.empty((p.B, p.H, p.Nq, p.d), dtype=dt, device=device)
+        b, _ = workspace_size(p, MCS_WS_BLOCK)
+        self.ws = torch.empty(max(b, 1), dtype=torch.uint8, device=device)
+
+    def step(self, Q, K, V, stream=None):
+        block_select(self.p, Q, K, self.perm, self.idx, self.ws, stream=stream)
+        sparse_attn(self.p, Q, K, V, self.perm, self.idx, None, self.O, stream=stream)
         return self.O

@@ -10,6 +10,10 @@ validated choice, so one near-tie cannot cascade:
     tokens whose oracle projection lies within 1e-5 * max|p| of the split point;
   * top-k: each group's selection must equal the oracle's, or else differ
     only in keys whose oracle mass is within 1e-5 relative of the k-th mass;
+  * block-sparse comparator: each query block's token list must equal the
+    oracle's, or else be whole blocks plus one partial block (its lowest
+    tokens) differing from the oracle's only in blocks whose oracle score lies
+    within 1e-5 * max|score| of the score of the oracle's last block taken;
   * outputs (O_full, R, reuse O): max|dO| <= 1e-2 * max|V| and
     mean|dO| <= 1e-3 * max|V| (bf16 inputs, fp32 accumulation).
 """
@@ -96,6 +100,38 @@ def check_topk(mass_oracle: np.ndarray, idx_gpu: np.ndarray, k: int, group: int)
         return None
     return (f"group {group}: {diff.size} keys differ, max |m - m_k| = {gap.max():.3e} "
             f"> {TOPK_BAND} * m_k = {TOPK_BAND * mk:.3e}")
+
+
+def check_block_selection(Q: np.ndarray, K: np.ndarray, idx_gpu: np.ndarray, g: int, G: int, k: int,
+                          scale: float, causal_block: int, q_offset: int, block: int = 64) -> Optional[str]:
+    """None if the GPU's block-sparse selection of query block g equals the
+    oracle's up to near-ties of the pooled block scores."""
+    Nq, Nkv = Q.shape[0], K.shape[0]
+    sel = np.asarray(idx_gpu, dtype=np.int64)
+    if sel.shape != (k,) or np.any(np.diff(sel) <= 0) or sel.min() < 0 or sel.max() >= Nkv:
+        return f"block {g}: selection is not {k} unique ascending in-range indices"
+    ora = orc.block_pooled_selection(Q, K, G, k, scale, causal_block, q_offset, block, groups=[g])[g]
+    if np.array_equal(sel, ora):
+        return None
+    nkb = -(-Nkv // block)
+    size = np.minimum(block, Nkv - block * np.arange(nkb))
+    got = np.bincount(sel // block, minlength=nkb)
+    want = np.bincount(ora // block, minlength=nkb)
+    part = np.flatnonzero((got > 0) & (got < size))
+    if part.size > 1 or any(sel[sel // block == b].tolist() != list(range(b * block, b * block + got[b]))
+                            for b in part):
+        return f"block {g}: selection is not whole blocks plus the lowest tokens of one block"
+    score = orc.block_scores(Q, K, orc.group_slices(Nq, G)[g], scale, causal_block, q_offset, block)
+    finite = score[np.isfinite(score)]
+    band = TOPK_BAND * (np.abs(finite).max() if finite.size else 1.0)
+    order = np.lexsort((np.arange(nkb), -score))
+    last = order[np.flatnonzero(want[order] > 0).max()]          # the oracle's last block taken
+    differ = np.flatnonzero(got != want)
+    gap = np.abs(score[differ] - score[last])
+    if np.all(np.isfinite(score[differ])) and np.isfinite(score[last]) and np.all(gap <= band):
+        return None
+    return (f"block {g}: {differ.size} KV blocks taken differently, max score gap to the boundary "
+            f"{np.nanmax(gap) if gap.size else 0.0:.3e} > band {band:.3e}")
 
 
 def compare(name: str, got: np.ndarray, ref: np.ndarray, vmax: float) -> StageReport:

@@ -113,3 +113,23 @@ def test_workspace_sizes():
     with pytest.raises(mcs.MCSError) as e:
         mcs.workspace_size(p, 9)
     assert e.value.status == mcs.MCS_ERR_INVALID_ARG
+
+
+def test_block_select_workspace_and_limits():
+    p = base()
+    b, bmin = mcs.workspace_size(p, mcs.MCS_WS_BLOCK)
+    # float32 pooled vectors: 16 query tiles and 19 key tiles of 2 heads
+    assert b == bmin == 4 * 2 * (16 + 19) * 128
+    with pytest.raises(mcs.MCSError) as e:      # workspace too small
+        mcs.block_select(p, 16, 16, 32, 48, 64, ws_bytes=b - 1, stream=0)
+    assert e.value.status == mcs.MCS_ERR_WORKSPACE
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.block_select(p, 16, 16, None, 48, 64, ws_bytes=b, stream=0)
+    assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "perm is NULL" in str(e.value)
+    with pytest.raises(mcs.MCSError) as e:      # 8193 KV blocks
+        mcs.block_select(base(Nkv=8193 * 64, k=10, d=64), 16, 16, 32, 48, 64, ws_bytes=1 << 40, stream=0)
+    assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
+    with pytest.raises(mcs.MCSError) as e:      # 513 blocks to rank (float32: no kept-key table limit)
+        mcs.block_select(base(Nkv=40000, k=32706, dtype="f32"), 16, 16, 32, 48, 64, ws_bytes=1 << 40, stream=0)
+    assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
+    mcs.block_select(base(Nq=0), None, None, None, None, None, ws_bytes=0, stream=0)
