@@ -8,7 +8,10 @@ steps' drifted inputs.  All inputs are generated up front and resident in HBM
 before the timed region.  Every library call is bracketed by HIP events on
 the stream the library launches on; the metric is the reuse step
 (mcs_sparse_attn).  The library's own exact attention (mcs_dense_attn) is
-timed on the same rotating inputs as the comparator.  Before every timed call
+timed on the same rotating inputs as the comparator, and so is the
+block-sparse comparator at the same token budget (mean-pooled block selection
+from each step's Q/K, mcs_block_select, then mcs_sparse_attn without a
+residual).  Before every timed call
 a 512 MB scratch buffer (twice the 256 MB Infinity Cache) is overwritten, so
 headline times are cold-cache; warm-cache times (back-to-back calls on one
 step's inputs) are reported beside them.
@@ -365,24 +368,55 @@ def main():
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dense_ms]
 
+    # block-sparse comparator at the same token budget: mean-pooled block
+    # selection from the step's own Q/K, then the gathered attention (no residual)
+    bsa = mcs.BlockSparseComparator(p)
+    bsa.step(*step_in[1], stream=stream)
+    torch.cuda.synchronize()
+    bsa_ev = []
+    for i in range(max(1, len(reuse_ms) // 2)):
+        s = 1 + i % (A - 1)
+        a, b, c = ev(), ev(), ev()
+        flush()
+        a.record(stream)
+        mcs.block_select(p, step_in[s][0], step_in[s][1], bsa.perm, bsa.idx, bsa.ws, stream=stream)
+        b.record(stream)
+        mcs.sparse_attn(p, *step_in[s], bsa.perm, bsa.idx, None, bsa.O, stream=stream)
+        c.record(stream)
+        bsa_ev.append((a, b, c))
+    torch.cuda.synchronize()
+    bsel_ms = [a.elapsed_time(b) for a, b, _ in bsa_ev]
+    bsa_ms = [a.elapsed_time(c) for a, _, c in bsa_ev]
+
     # fidelity diagnostic (untimed): relative error of the reuse output against the
     # library's exact attention on the same step, with and without the residual, by
     # steps since the anchor (the last timed period's anchor state is still in place)
-    fid_r, fid_nor, fid_stale = [], [], []
+    # Also: the block-sparse comparator recomputed on the step, and the exact
+    # token selection recomputed on the step (an anchor on that step's inputs,
+    # its sparse output without the residual): together they separate the
+    # errors of block-granular pooled selection, of selection staleness and of
+    # the discarded tail.
+    fid_r, fid_nor, fid_stale, fid_bsa, fid_now = [], [], [], [], []
     if not args.no_fidelity:
         On = torch.empty_like(st.O)
         O0 = torch.empty_like(st.O)
+        now = mcs.MCSparseAttention(p)
         mcs.dense_attn(p, *step_in[0], O0, stream=stream)  # the anchor step's exact output
         for s in range(1, A):
             mcs.dense_attn(p, *step_in[s], Od, stream=stream)
-            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
-            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, None, On, stream=stream)
             ref = Od.float()
             nrm = ref.norm().item()
-            fid_r.append(round((st.O.float() - ref).norm().item() / nrm, 6))
-            fid_nor.append(round((On.float() - ref).norm().item() / nrm, 6))
-            fid_stale.append(round((O0.float() - ref).norm().item() / nrm, 6))
-        del On, O0
+            rel = lambda O: round((O.float() - ref).norm().item() / nrm, 6)  # noqa: E731
+            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
+            fid_r.append(rel(st.O))
+            mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, None, On, stream=stream)
+            fid_nor.append(rel(On))
+            fid_stale.append(rel(O0))
+            fid_bsa.append(rel(bsa.step(*step_in[s], stream=stream)))
+            now.step(*step_in[s], True, stream=stream)
+            mcs.sparse_attn(p, *step_in[s], now.perm, now.idx, None, On, stream=stream)
+            fid_now.append(rel(On))
+        del On, O0, now
         torch.cuda.synchronize()
 
     # warm cache: back-to-back calls on one step's inputs, no flush
@@ -463,6 +497,10 @@ def main():
         "fidelity_rel_err_with_R": fid_r or None,
         "fidelity_rel_err_without_R": fid_nor or None,
         "fidelity_rel_err_stale_anchor_output": fid_stale or None,
+        "fidelity_rel_err_block_sparse_recomputed": fid_bsa or None,
+        "fidelity_rel_err_exact_selection_recomputed_without_R": fid_now or None,
+        "block_sparse_ms_per_call": round(statistics.fmean(bsa_ms), 4),
+        "block_select_ms_per_call": round(statistics.fmean(bsel_ms), 4),
         "reuse_ms_warm_median": round(statistics.median(warm_ms), 4) if warm else None,
         "hbm_copy_gbs_measured": round(copy_gbs, 1),
         "device_cus": cus,

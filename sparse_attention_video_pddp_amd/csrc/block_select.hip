@@ -16,12 +16,16 @@
 // then gives its lowest-index tokens up to exactly k.  The token lists are
 // written ascending and feed the gathered sparse attention unchanged.
 //
-// Kernels: pool_kernel (one workgroup per tile of Q or K: fp32 sums in a
-// fixed order, then the mean; one read of Q and K) and block_select_kernel
-// (one workgroup per query block: the block scores in LDS as order keys, the
-// block select of select.hpp for the top J = min(nkb, ceil((k-1)/64) + 1)
-// blocks, which always hold at least k tokens, then a rank walk over those J
-// and the token emission).
+// Kernels.  pool_kernel: one workgroup per tile of Q or K, fp32 sums in a
+// fixed order, then the mean (one read of Q and K).  The select kernels run
+// one workgroup per query block.  Scores: eight lanes per pooled key row
+// (coalesced 512-byte rows, all loads of a pass in flight), summed in a fixed
+// butterfly.  Ranking: with at most kSortBlocks KV blocks, a bitonic sort in
+// LDS of (score key, block index) pairs; beyond, the radix block select of
+// select.hpp for the top J = min(nkb, ceil((k-1)/64) + 1) blocks (which always
+// hold at least k tokens) followed by an exact ranking of those J.  The token
+// counts of the ranked blocks come from one scan of their sizes, their output
+// offsets from one scan in block-index order.
 #include "mcs_kernels.hpp"
 #include "select.hpp"
 
@@ -29,6 +33,7 @@ namespace mcs {
 namespace {
 
 constexpr int kSelThreads = 256;
+constexpr int kSortBlocks = 4096;  // bitonic path limit (32 KB of pairs)
 
 struct PoolParams {
   const void *Q, *K;
@@ -36,25 +41,29 @@ struct PoolParams {
   int Nq, Nkv, G, c, nkb, BH;
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
-    const bf16x4 x = *(const bf16x4*)p;
+    const bf16x8 x = *(const bf16x8*)p;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (float)x[e];
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
   } else {
-    const f32x4 x = *(const f32x4*)p;
+    const f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = x[e];
+    for (int e = 0; e < 4; ++e) {
+      v[e] = x0[e];
+      v[4 + e] = x1[e];
+    }
   }
 }
 
 // Workgroups [0, BH*c) pool query tiles, the rest key tiles.  Thread
-// (r, c4) sums channels 4*c4..4*c4+3 over rows r, r + RP, ...; the RP
-// partial sums are then added in row-slot order.
+// (r, c8) sums channels 8*c8..8*c8+7 over rows r, r + RP, ... (16-byte loads
+// of bf16, all of a thread's rows in flight); the RP partial sums are then
+// added in row-slot order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
-  constexpr int C4 = D / 4, RP = 256 / C4;
+  constexpr int C8 = D / 8, RP = 256 / C8, MAXR = 128 / RP;  // tiles have at most 128 rows
   __shared__ float part[RP][D];
   int unit = blockIdx.x;
   const T* src;
@@ -74,16 +83,23 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     src = (const T*)p.K + (size_t)bh * p.Nkv * D;
     dst = p.kbar + (size_t)unit * D;
   }
-  const int r = threadIdx.x / C4, c4 = threadIdx.x - r * C4;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int row = r0 + r; row < r1; row += RP) {
-    float v[4];
-    load4<T, D>(src + (size_t)row * D + 4 * c4, v);
+  const int r = threadIdx.x / C8, c8 = threadIdx.x - r * C8;
+  float v[MAXR][8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += v[e];
-  }
+  for (int i = 0; i < MAXR; ++i)
+    if (i * RP < r1 - r0) {  // uniform; within it, rows past the tile are clamped, loaded and not added
+      const int row = min(r0 + r + i * RP, r1 - 1);
+      load8<T>(src + (size_t)row * D + 8 * c8, v[i]);
+    }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) part[r][4 * c4 + e] = acc[e];
+  for (int i = 0; i < MAXR; ++i)
+    if (r0 + r + i * RP < r1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[i][e];
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r][8 * c8 + e] = acc[e];
   __syncthreads();
   if (threadIdx.x < D) {
     float s = 0.f;
@@ -96,7 +112,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 struct SelectParams {
   const float *qbar, *kbar;
   int32_t *perm, *idx;
-  int Nq, Nkv, G, k, c, nkb, J;
+  int Nq, Nkv, G, k, c, nkb, J, npad;
   float scale;
   int causal_block, q_offset;
 };
@@ -106,38 +122,186 @@ struct LdsKeys {
   __device__ __forceinline__ uint32_t operator()(int j) const { return a[j]; }
 };
 
+// Identity grouping of this query block and its pooled vector into LDS.
 template <int D>
-__global__ __launch_bounds__(kSelThreads) void block_select_kernel(SelectParams p) {
-  using Sel = BlockSelect<kSelThreads, 0>;
-  __shared__ typename Sel::Shared sh;
-  __shared__ uint32_t keys[kMaxKvBlocks];
-  __shared__ __attribute__((aligned(16))) float qb[D];
-  __shared__ int s_blk[kMaxSelBlocks], s_cnt[kMaxSelBlocks], s_off[kMaxSelBlocks], s_order[kMaxSelBlocks];
-  __shared__ uint32_t s_key[kMaxSelBlocks];
-  const int unit = blockIdx.x;
+__device__ __forceinline__ void select_prologue(const SelectParams& p, int unit, float* qb) {
   const int bh = unit / p.c, g = unit - bh * p.c;
-  const int tid = threadIdx.x;
   const int q0 = g * p.G, q1 = min(q0 + p.G, p.Nq);
-  for (int i = tid; i < q1 - q0; i += kSelThreads) p.perm[(size_t)bh * p.Nq + q0 + i] = q0 + i;
-  if (tid < D) qb[tid] = p.qbar[(size_t)unit * D + tid];
+  for (int i = threadIdx.x; i < q1 - q0; i += kSelThreads) p.perm[(size_t)bh * p.Nq + q0 + i] = q0 + i;
+  if (threadIdx.x < D) qb[threadIdx.x] = p.qbar[(size_t)unit * D + threadIdx.x];
   __syncthreads();
+}
+
+// Order key of every KV block's score (0 for a block with no visible key,
+// below every score); put(b, key) for b < nkb.  Eight lanes share a row: lane
+// `sub` multiplies channels [sub*D/8, (sub+1)*D/8) in order, then the eight
+// partial sums meet in a fixed butterfly.
+template <int D, class Put>
+__device__ __forceinline__ void block_scores(const SelectParams& p, int unit, const float* qb, Put&& put) {
+  constexpr int LPR = 8, CPL = D / LPR, RPP = kSelThreads / LPR, U = 4;
+  const int bh = unit / p.c, g = unit - bh * p.c;
+  const int q1 = min(g * p.G + p.G, p.Nq);
   // the last query of the block sees the most keys (limits are nondecreasing)
   const int lim = visible_limit(q1 - 1, p.causal_block, p.q_offset, p.Nkv);
-  for (int b = tid; b < p.nkb; b += kSelThreads) {
-    const float* kr = p.kbar + ((size_t)bh * p.nkb + b) * D;
-    float s = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < D; e += 4) {
-      const f32x4 kv = *(const f32x4*)(kr + e);
-      const f32x4 qv = *(const f32x4*)(qb + e);
-      s = fmaf(qv[0], kv[0], s);
-      s = fmaf(qv[1], kv[1], s);
-      s = fmaf(qv[2], kv[2], s);
-      s = fmaf(qv[3], kv[3], s);
+  const int sub = threadIdx.x & (LPR - 1), rr = threadIdx.x / LPR;
+  float qv[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) qv[i] = qb[sub * CPL + i];
+  const float* kh = p.kbar + (size_t)bh * p.nkb * D + sub * CPL;
+  for (int b0 = 0; b0 < p.nkb; b0 += RPP * U) {
+    float part[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = min(b0 + u * RPP + rr, p.nkb - 1);
+      const f32x4* kr = (const f32x4*)(kh + (size_t)b * D);
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL / 4; ++i) {
+        const f32x4 v = kr[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum = fmaf(qv[4 * i + e], v[e], sum);
+      }
+      part[u] = sum;
     }
-    // order key of the score; blocks with no visible key take 0, below every score
-    keys[b] = b * kPoolBlock < lim ? float_order_key(s * p.scale + 0.f) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float sum = part[u];
+      sum += __shfl_xor(sum, 1, 64);
+      sum += __shfl_xor(sum, 2, 64);
+      sum += __shfl_xor(sum, 4, 64);
+      const int b = b0 + u * RPP + rr;
+      if (sub == 0 && b < p.nkb) put(b, b * kPoolBlock < lim ? float_order_key(sum * p.scale + 0.f) : 0u);
+    }
   }
+}
+
+// Token counts of the J ranked blocks (rank r: block blk[r], kPoolBlock
+// tokens but the last block's), taken in rank order up to k in all:
+// cnt[r].  sw: scan scratch.  Ends with a barrier.
+__device__ __forceinline__ void rank_counts(const SelectParams& p, const int* blk, int* cnt, int* sw) {
+  const int tid = threadIdx.x;
+  int sz[2], tot;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 2 * tid + h;
+    sz[h] = r < p.J ? min(kPoolBlock, p.Nkv - blk[r] * kPoolBlock) : 0;
+  }
+  int run = block_excl_scan<kSelThreads>(sz[0] + sz[1], sw, tot);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 2 * tid + h;
+    if (r < p.J) cnt[r] = max(0, min(sz[h], p.k - run));
+    run += sz[h];
+  }
+  __syncthreads();
+}
+
+// Exclusive scan of n <= PER * kSelThreads ints (PER contiguous per thread)
+// into out.  Ends with a barrier.
+template <int PER, class In>
+__device__ __forceinline__ void scan_blocked(int n, In&& in, int* out, int* sw) {
+  int loc[PER], s = 0, tot;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = PER * threadIdx.x + i;
+    loc[i] = b < n ? in(b) : 0;
+    s += loc[i];
+  }
+  int off = block_excl_scan<kSelThreads>(s, sw, tot);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = PER * threadIdx.x + i;
+    if (b < n) out[b] = off;
+    off += loc[i];
+  }
+  __syncthreads();
+}
+
+// Tokens of J chosen blocks: entry i is block blocks[i], cnts[i] tokens
+// written from offs[i].  One wave per entry, lane t its t-th token.
+__device__ __forceinline__ void emit_tokens(const SelectParams& p, int unit, const int* blocks, const int* cnts,
+                                            const int* offs) {
+  int32_t* out = p.idx + (size_t)unit * p.k;
+  const int t = threadIdx.x & 63;
+  for (int i = threadIdx.x >> 6; i < p.J; i += kSelThreads / 64)
+    if (t < cnts[i]) out[offs[i] + t] = blocks[i] * kPoolBlock + t;
+}
+
+// Descending bitonic sort of n (a power of two) 64-bit values in LDS.
+__device__ __forceinline__ void bitonic_sort_desc(unsigned long long* a, int n) {
+  for (int size = 2; size <= n; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int q = threadIdx.x; q < n / 2; q += kSelThreads) {
+        const int i = 2 * stride * (q / stride) + (q % stride), j = i + stride;
+        const bool desc = (i & size) == 0;  // the final merge (size == n) is descending throughout
+        const unsigned long long x = a[i], y = a[j];
+        if ((x < y) == desc) {
+          a[i] = y;
+          a[j] = x;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// Up to kSortBlocks KV blocks.  Dynamic LDS: npad 64-bit (key, ~block)
+// pairs, reused after the sort for per-block counts and offsets [nkb] each;
+// then three arrays of J: ranked blocks, their counts and output offsets.
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void block_select_sort_kernel(SelectParams p) {
+  __shared__ __attribute__((aligned(16))) float qb[D];
+  __shared__ int sw[kSelThreads / 64];
+  extern __shared__ unsigned long long dyn64[];
+  unsigned long long* comp = dyn64;
+  int* blk = (int*)(dyn64 + p.npad);
+  int* cnt = blk + p.J;
+  int* offr = cnt + p.J;
+  const int unit = blockIdx.x;
+  select_prologue<D>(p, unit, qb);
+  // higher key first, then lower block index; padding (0) sorts last
+  for (int b = p.nkb + threadIdx.x; b < p.npad; b += kSelThreads) comp[b] = 0ull;
+  block_scores<D>(p, unit, qb, [&](int b, uint32_t key) {
+    comp[b] = ((unsigned long long)key << 32) | (0xFFFFFFFFu - (uint32_t)b);
+  });
+  __syncthreads();
+  bitonic_sort_desc(comp, p.npad);
+  for (int r = threadIdx.x; r < p.J; r += kSelThreads) blk[r] = (int)(0xFFFFFFFFu - (uint32_t)comp[r]);
+  __syncthreads();
+  rank_counts(p, blk, cnt, sw);
+  // output offsets in block-index order: counts scattered by block, one scan
+  int* cntb = (int*)comp;
+  int* offb = cntb + p.nkb;
+  for (int b = threadIdx.x; b < p.nkb; b += kSelThreads) cntb[b] = 0;
+  __syncthreads();
+  for (int r = threadIdx.x; r < p.J; r += kSelThreads) cntb[blk[r]] = cnt[r];
+  __syncthreads();
+  scan_blocked<kSortBlocks / kSelThreads>(p.nkb, [&](int b) { return cntb[b]; }, offb, sw);
+  for (int r = threadIdx.x; r < p.J; r += kSelThreads) offr[r] = offb[blk[r]];
+  __syncthreads();
+  emit_tokens(p, unit, blk, cnt, offr);
+}
+
+// More than kSortBlocks KV blocks (up to kMaxKvBlocks).  Dynamic LDS: keys
+// [nkb], then six arrays of J: the selected blocks in index order, their
+// keys, their ranks, the blocks in rank order, the counts by rank, and
+// counts then offsets in index order.
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void block_select_radix_kernel(SelectParams p) {
+  using Sel = BlockSelect<kSelThreads, 0>;
+  __shared__ typename Sel::Shared sh;
+  __shared__ __attribute__((aligned(16))) float qb[D];
+  extern __shared__ uint32_t dyn[];
+  uint32_t* keys = dyn;
+  int* s_sel = (int*)(keys + p.nkb);
+  uint32_t* s_key = (uint32_t*)(s_sel + p.J);
+  int* rk = (int*)(s_key + p.J);
+  int* blk = rk + p.J;
+  int* cnt = blk + p.J;
+  int* cnte = cnt + p.J;
+  int* offe = (int*)s_key;  // the keys are no longer needed once the counts are known
+  const int unit = blockIdx.x;
+  select_prologue<D>(p, unit, qb);
+  block_scores<D>(p, unit, qb, [&](int b, uint32_t key) { keys[b] = key; });
   __syncthreads();
   const LdsKeys kf{keys};
   Sel sel;
@@ -147,40 +311,26 @@ __global__ __launch_bounds__(kSelThreads) void block_select_kernel(SelectParams 
   sel.threshold(kf, p.J, sh, T, tie_need);
   sel.split(kf, T, tie_need, sh, [&](int, int j, bool s, int pos) {
     if (s && pos < p.J) {
-      s_blk[pos] = j;
+      s_sel[pos] = j;
       s_key[pos] = keys[j];
     }
   });
   __syncthreads();
-  // score rank of each of the J blocks (they are in index order, so a lower
-  // position is a lower block index)
-  for (int e = tid; e < p.J; e += kSelThreads) {
+  // rank of each selected block by (key desc, index asc); they are in index
+  // order, so a lower position is a lower block index
+  for (int e = threadIdx.x; e < p.J; e += kSelThreads) {
     const uint32_t ke = s_key[e];
     int r = 0;
     for (int f = 0; f < p.J; ++f) r += (s_key[f] > ke) || (s_key[f] == ke && f < e);
-    s_order[r] = e;
+    rk[e] = r;
+    blk[r] = s_sel[e];
   }
   __syncthreads();
-  if (tid == 0) {
-    int tot = 0;
-    for (int r = 0; r < p.J; ++r) {
-      const int e = s_order[r];
-      const int size = min(kPoolBlock, p.Nkv - s_blk[e] * kPoolBlock);
-      const int cnt = min(size, p.k - tot);
-      s_cnt[e] = cnt;
-      tot += cnt;
-    }
-    int off = 0;
-    for (int e = 0; e < p.J; ++e) {
-      s_off[e] = off;
-      off += s_cnt[e];
-    }
-  }
+  rank_counts(p, blk, cnt, sh.cnt_eq);
+  for (int e = threadIdx.x; e < p.J; e += kSelThreads) cnte[e] = cnt[rk[e]];
   __syncthreads();
-  int32_t* out = p.idx + (size_t)unit * p.k;
-  const int t = tid & (kPoolBlock - 1);
-  for (int e = tid / kPoolBlock; e < p.J; e += kSelThreads / kPoolBlock)
-    if (t < s_cnt[e]) out[s_off[e] + t] = s_blk[e] * kPoolBlock + t;
+  scan_blocked<kMaxSelBlocks / kSelThreads>(p.J, [&](int e) { return cnte[e]; }, offe, sh.cnt_eq);
+  emit_tokens(p, unit, s_sel, cnte, offe);
 }
 
 }  // namespace
@@ -206,9 +356,19 @@ hipError_t launch_block_select(const Shape& s, bool bf16, const void* Q, const v
   sp.Nq = s.Nq; sp.Nkv = s.Nkv; sp.G = s.G; sp.k = s.k; sp.c = s.c; sp.nkb = nkb;
   sp.J = block_select_count(s.k, nkb);
   sp.scale = s.scale; sp.causal_block = s.causal_block; sp.q_offset = s.q_offset;
+  int npad = 64;
+  while (npad < nkb) npad *= 2;
+  sp.npad = npad;
   const dim3 sgrid((unsigned)((long long)s.BH * s.c));
-  if (s.d == 128) hipLaunchKernelGGL(block_select_kernel<128>, sgrid, dim3(kSelThreads), 0, st, sp);
-  else hipLaunchKernelGGL(block_select_kernel<64>, sgrid, dim3(kSelThreads), 0, st, sp);
+  if (nkb <= kSortBlocks) {
+    const size_t lds = (size_t)npad * 8 + (size_t)sp.J * 12;  // <= 38 KB
+    if (s.d == 128) hipLaunchKernelGGL(block_select_sort_kernel<128>, sgrid, dim3(kSelThreads), lds, st, sp);
+    else hipLaunchKernelGGL(block_select_sort_kernel<64>, sgrid, dim3(kSelThreads), lds, st, sp);
+  } else {
+    const size_t lds = ((size_t)nkb + (size_t)sp.J * 6) * 4;  // <= 44 KB (+ 18 KB static)
+    if (s.d == 128) hipLaunchKernelGGL(block_select_radix_kernel<128>, sgrid, dim3(kSelThreads), lds, st, sp);
+    else hipLaunchKernelGGL(block_select_radix_kernel<64>, sgrid, dim3(kSelThreads), lds, st, sp);
+  }
   return hipGetLastError();
 }
 

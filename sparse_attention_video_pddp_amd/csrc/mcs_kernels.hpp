@@ -58,7 +58,7 @@ inline __host__ __device__ int block_select_count(int k, int nkb) {
   const int j = (k - 1 + kPoolBlock - 1) / kPoolBlock + 1;
   return j < nkb ? j : nkb;
 }
-// ws: float32 pooled queries [BH*c*d] then pooled keys [BH*nkb*d].
+// ws: float32 pooled queries [BH][c][d] then pooled keys [BH][d][nkb].
 size_t block_workspace_bytes(const Shape& s);
 hipError_t launch_block_select(const Shape& s, bool bf16, const void* Q, const void* K, int32_t* perm,
                                int32_t* idx, void* ws, hipStream_t st);

@@ -99,3 +99,22 @@ def test_block_sparse_full_size_sampled(cuda, name):
     for (b, h) in heads:
         mx, mn = _check_head(w, cmp_, O, host, b, h, groups)
         log(f"  {name} head {(b, h)} blocks {groups}: ok, O max|d|={mx:.3e} mean|d|={mn:.3e}")
+
+
+LONG = {
+    # 196608 keys -> 3072 KV blocks: the sort path at its largest padding (4096 pairs)
+    "long_kv_sort": synth.get("stress").with_(name="long_kv_sort", H=1, grid=(48, 64, 64)),
+    # 270336 keys -> 4224 KV blocks: beyond the sort path, the radix block select
+    "long_kv_radix": synth.get("stress").with_(name="long_kv_radix", H=1, grid=(66, 64, 64)),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG))
+def test_block_sparse_long_kv_sampled(cuda, name):
+    from tests.gpu_runner import log
+    w = LONG[name]
+    cmp_, O, host, _ = _run(w, 1, [(0, 0)])
+    rng = np.random.default_rng(11)
+    groups = sorted({0, w.n_groups - 1, *rng.choice(w.n_groups, 3, replace=False).tolist()})
+    mx, mn = _check_head(w, cmp_, O, host, 0, 0, groups)
+    log(f"  {name} ({-(-w.Nkv // 64)} KV blocks) blocks {groups}: ok, O max|d|={mx:.3e} mean|d|={mn:.3e}")
