@@ -235,6 +235,31 @@ def topk_select(mass: np.ndarray, k: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Residual-drift check (adaptive anchoring)
+# ---------------------------------------------------------------------------
+def sampled_drift(O, Q, K, V, rows, scale: float, causal_block: int = 0, q_offset: int = 0) -> float:
+    """Relative distance of a step's output from exact attention on sampled
+    query rows: ||O[rows] - O_exact[rows]||_F / ||O_exact[rows]||_F (0 when
+    the exact rows are all zero).
+
+    For a reuse output O = O_sparse + R_anchor, O - O_exact equals
+    R_anchor - R_now, the movement of the dense-sparse residual since the
+    anchor, measured against the output.  The review page (section 3) reuses
+    selections and the residual because both are temporally stable; this is
+    the quantity whose growth says that they no longer are, read here as the
+    trigger for the next anchor.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    Q, K, V = _as64(Q), _as64(K), _as64(V)
+    ex = np.zeros((rows.size, V.shape[1]), _F)
+    for n, r in enumerate(rows):   # each sampled row at its own position q_offset + r
+        ex[n] = dense_attention(Q[r:r + 1], K, V, scale, causal_block, q_offset + int(r))[0][0]
+    ref = float(np.sqrt((ex ** 2).sum()))
+    err = float(np.sqrt(((_as64(O)[rows] - ex) ** 2).sum()))
+    return err / ref if ref > 0 else 0.0
+
+
+# ---------------------------------------------------------------------------
 # Block-sparse comparator: mean-pooled block selection
 # ---------------------------------------------------------------------------
 def block_scores(Q, K, rows: slice, scale: float, causal_block: int = 0, q_offset: int = 0,

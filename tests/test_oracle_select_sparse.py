@@ -156,3 +156,46 @@ def test_reuse_adds_residual_to_sparse_output():
     R = rng.standard_normal((nq, 8))
     O = reuse_step(Q, K, V, perm, idx, R, G, 1.0)
     np.testing.assert_allclose(O - R, sparse_attention(Q, K, V, perm, idx, G, 1.0), atol=1e-14)
+
+
+# --- residual-drift check (adaptive anchoring) ------------------------------
+from oracle.mcs_oracle import sampled_drift  # noqa: E402
+
+
+def test_drift_on_all_rows_is_the_relative_error():
+    rng = np.random.default_rng(21)
+    Q, K, V = rng.standard_normal((40, 8)), rng.standard_normal((50, 8)), rng.standard_normal((50, 8))
+    Od, _ = dense_attention(Q, K, V, 0.4, 10, 5)
+    O = Od + 0.01 * rng.standard_normal(Od.shape)
+    rel = np.linalg.norm(O - Od) / np.linalg.norm(Od)
+    assert abs(sampled_drift(O, Q, K, V, np.arange(40), 0.4, 10, 5) - rel) < 1e-12
+    assert sampled_drift(Od, Q, K, V, [3, 17, 39], 0.4, 10, 5) < 1e-14
+
+
+def test_drift_hand_example():
+    # two keys, equal logits for row 0: exact output = mean of the values
+    Q = np.array([[0.0, 0.0], [1.0, 0.0]])
+    K = np.array([[1.0, 0.0], [-1.0, 0.0]])
+    V = np.array([[2.0, 0.0], [0.0, 2.0]])
+    O = np.array([[1.0, 1.0 + 0.3], [9.0, 9.0]])
+    # row 0 exact (1, 1): error 0.3, norm sqrt(2)
+    assert abs(sampled_drift(O, Q, K, V, [0], 1.0) - 0.3 / math.sqrt(2.0)) < 1e-12
+    # causal frames of one token: row 0 at position 0 sees key 0 only -> exact (2, 0)
+    assert abs(sampled_drift(O, Q, K, V, [0], 1.0, causal_block=1) - math.hypot(1.0, 1.3) / 2.0) < 1e-12
+
+
+def test_drift_of_the_reuse_output_is_the_residual_movement():
+    """At the anchor step itself the reuse output is the dense output (drift 0);
+    on a later step it is |R_anchor - R_now| relative to the output."""
+    rng = np.random.default_rng(22)
+    Q, K, V = rng.standard_normal((130, 8)), rng.standard_normal((130, 8)), rng.standard_normal((130, 8))
+    a = anchor_step(Q, K, V, 64, 20, 0.5, iters=8)
+    rows = np.arange(0, 130, 7)
+    O0 = reuse_step(Q, K, V, a["perm"], a["idx"], a["R"], 64, 0.5)
+    assert sampled_drift(O0, Q, K, V, rows, 0.5) < 1e-12
+    Q1, K1, V1 = (x + 0.1 * rng.standard_normal(x.shape) for x in (Q, K, V))
+    O1 = reuse_step(Q1, K1, V1, a["perm"], a["idx"], a["R"], 64, 0.5)
+    Od1, _ = dense_attention(Q1, K1, V1, 0.5)
+    R_now = Od1 - sparse_attention(Q1, K1, V1, a["perm"], a["idx"], 64, 0.5)
+    want = np.linalg.norm((a["R"] - R_now)[rows]) / np.linalg.norm(Od1[rows])
+    assert abs(sampled_drift(O1, Q1, K1, V1, rows, 0.5) - want) < 1e-12
