@@ -11,7 +11,8 @@ the stream the library launches on; the metric is the reuse step
 timed on the same rotating inputs as the comparator, and so is the
 block-sparse comparator at the same token budget (mean-pooled block selection
 from each step's Q/K, mcs_block_select, then mcs_sparse_attn without a
-residual).  Before every timed call
+residual), and the residual-drift check of adaptive anchoring
+(mcs_residual_drift, 64 sampled rows per head).  Before every timed call
 a 512 MB scratch buffer (twice the 256 MB Infinity Cache) is overwritten, so
 headline times are cold-cache; warm-cache times (back-to-back calls on one
 step's inputs) are reported beside them.
@@ -388,6 +389,25 @@ def main():
     bsel_ms = [a.elapsed_time(b) for a, b, _ in bsa_ev]
     bsa_ms = [a.elapsed_time(c) for a, _, c in bsa_ev]
 
+    # residual-drift check of adaptive anchoring (64 sampled rows per head) on
+    # a reuse output, same cold protocol
+    drift_rows = torch.tensor(mcs.drift_rows(w.Nq, 64), dtype=torch.int32, device=dev)
+    drift = torch.zeros((w.B, w.H), dtype=torch.float32, device=dev)
+    ws_drift = torch.empty(max(mcs.workspace_size(p, mcs.MCS_WS_DRIFT)[0], 1), dtype=torch.uint8, device=dev)
+    mcs.residual_drift(p, *step_in[1], st.O, drift_rows, drift, ws_drift, stream=stream)
+    torch.cuda.synchronize()
+    drift_ev = []
+    for i in range(max(1, len(reuse_ms) // 2)):
+        s = 1 + i % (A - 1)
+        a, b = ev(), ev()
+        flush()
+        a.record(stream)
+        mcs.residual_drift(p, *step_in[s], st.O, drift_rows, drift, ws_drift, stream=stream)
+        b.record(stream)
+        drift_ev.append((a, b))
+    torch.cuda.synchronize()
+    drift_ms = [a.elapsed_time(b) for a, b in drift_ev]
+
     # fidelity diagnostic (untimed): relative error of the reuse output against the
     # library's exact attention on the same step, with and without the residual, by
     # steps since the anchor (the last timed period's anchor state is still in place)
@@ -396,7 +416,7 @@ def main():
     # its sparse output without the residual): together they separate the
     # errors of block-granular pooled selection, of selection staleness and of
     # the discarded tail.
-    fid_r, fid_nor, fid_stale, fid_bsa, fid_now = [], [], [], [], []
+    fid_r, fid_nor, fid_stale, fid_bsa, fid_now, fid_drift = [], [], [], [], [], []
     if not args.no_fidelity:
         On = torch.empty_like(st.O)
         O0 = torch.empty_like(st.O)
@@ -409,6 +429,8 @@ def main():
             rel = lambda O: round((O.float() - ref).norm().item() / nrm, 6)  # noqa: E731
             mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
             fid_r.append(rel(st.O))
+            mcs.residual_drift(p, *step_in[s], st.O, drift_rows, drift, ws_drift, stream=stream)
+            fid_drift.append(round(float(drift.max().item()), 6))
             mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, None, On, stream=stream)
             fid_nor.append(rel(On))
             fid_stale.append(rel(O0))
@@ -501,6 +523,8 @@ def main():
         "fidelity_rel_err_exact_selection_recomputed_without_R": fid_now or None,
         "block_sparse_ms_per_call": round(statistics.fmean(bsa_ms), 4),
         "block_select_ms_per_call": round(statistics.fmean(bsel_ms), 4),
+        "drift_check_ms_per_call": round(statistics.fmean(drift_ms), 4),
+        "drift_sampled_max_over_heads": fid_drift or None,
         "reuse_ms_warm_median": round(statistics.median(warm_ms), 4) if warm else None,
         "hbm_copy_gbs_measured": round(copy_gbs, 1),
         "device_cus": cus,

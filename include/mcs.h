@@ -57,7 +57,8 @@ typedef enum mcs_dtype { MCS_F32 = 0, MCS_BF16 = 1 } mcs_dtype;
 typedef enum mcs_workspace_kind {
   MCS_WS_GROUP = 0,
   MCS_WS_ANCHOR = 1,
-  MCS_WS_BLOCK = 2
+  MCS_WS_BLOCK = 2,
+  MCS_WS_DRIFT = 3
 } mcs_workspace_kind;
 
 /* Problem description.  Supported: d in {64,128}; group_size in {64,128};
@@ -80,8 +81,9 @@ typedef struct mcs_problem {
 } mcs_problem;
 
 /* Bytes of workspace mcs_group (kind MCS_WS_GROUP), mcs_anchor
- * (MCS_WS_ANCHOR) or mcs_block_select (MCS_WS_BLOCK) needs to process all B*H
- * heads in one pass.  For
+ * (MCS_WS_ANCHOR), mcs_block_select (MCS_WS_BLOCK) or mcs_residual_drift
+ * (MCS_WS_DRIFT, sized for its largest n_rows) needs to process all B*H heads
+ * in one pass.  For
  * MCS_WS_ANCHOR any size of at least `*min_bytes` works (heads are then
  * processed in chunks); min_bytes may be NULL.  For bf16 problems the anchor
  * workspace also holds the float32 O_full of all heads (B*H*Nq*d*4 bytes, part
@@ -164,6 +166,26 @@ mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, c
  * or k > 32705 (more than 512 blocks to rank). */
 mcs_status mcs_block_select(const mcs_problem* p, const void* Q, const void* K, int32_t* perm, int32_t* idx,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Residual-drift check for adaptive anchoring (MC-Sparse review, section 3:
+ * selections and the dense-sparse residual are reused because they are
+ * temporally stable; this measures how far they have moved).  For every head
+ * the sampled query rows get exact attention in float32 (split over key
+ * ranges), and
+ *   drift[b,h] = ||O[rows] - O_exact[rows]||_F / ||O_exact[rows]||_F
+ * (0 when O_exact is 0 on every sampled row), O being the caller's output for
+ * this step.  For a reuse output O = O_sparse + R_anchor this is the movement
+ * of the residual since the anchor, R_anchor - R_now, relative to the output;
+ * a caller anchors again when it exceeds a threshold.
+ *   O      [B,H,Nq,d] dtype, read (the step's output, e.g. from mcs_sparse_attn).
+ *   rows   [n_rows] int32 device memory: token indices in [0,Nq), the same
+ *          for every head (clamped into range on the device).
+ *   n_rows 1..128.
+ *   drift  [B,H] float32 device memory, written.
+ *   ws     workspace of at least mcs_workspace_size(MCS_WS_DRIFT) bytes. */
+mcs_status mcs_residual_drift(const mcs_problem* p, const void* Q, const void* K, const void* V, const void* O,
+                              const int32_t* rows, int32_t n_rows, float* drift, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* Static description of a status code. */
 const char* mcs_status_string(mcs_status s);

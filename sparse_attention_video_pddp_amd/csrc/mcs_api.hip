@@ -160,6 +160,8 @@ mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes,
     }
   } else if (kind == MCS_WS_BLOCK) {
     need = need_min = c.empty ? 0 : mcs::block_workspace_bytes(c.s);
+  } else if (kind == MCS_WS_DRIFT) {
+    need = need_min = c.empty ? 0 : mcs::drift_workspace_bytes(c.s);
   } else {
     return fail(MCS_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
   }
@@ -249,6 +251,23 @@ mcs_status mcs_block_select(const mcs_problem* p, const void* Q, const void* K, 
     return s;
   return hip_status(mcs::launch_block_select(c.s, c.bf16, Q, K, perm, idx, ws, (hipStream_t)stream),
                     "mcs_block_select");
+}
+
+mcs_status mcs_residual_drift(const mcs_problem* p, const void* Q, const void* K, const void* V, const void* O,
+                              const int32_t* rows, int32_t n_rows, float* drift, void* ws, size_t ws_bytes,
+                              void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (n_rows < 1 || n_rows > mcs::kMaxDriftRows)
+    return fail(MCS_ERR_INVALID_ARG, "n_rows=%d outside [1, %d]", n_rows, mcs::kMaxDriftRows);
+  if (c.empty) return ok();
+  const size_t need = mcs::drift_workspace_bytes(c.s);
+  if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "drift workspace %zu < %zu bytes", ws_bytes, need);
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {O, "O", false},
+                                 {rows, "rows", false}, {drift, "drift", false}, {ws, "ws", false}}))
+    return s;
+  return hip_status(mcs::launch_drift(c.s, c.bf16, Q, K, V, O, rows, n_rows, drift, ws, (hipStream_t)stream),
+                    "mcs_residual_drift");
 }
 
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,

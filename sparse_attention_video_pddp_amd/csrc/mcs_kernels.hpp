@@ -63,6 +63,14 @@ size_t block_workspace_bytes(const Shape& s);
 hipError_t launch_block_select(const Shape& s, bool bf16, const void* Q, const void* K, int32_t* perm,
                                int32_t* idx, void* ws, hipStream_t st);
 
+// Residual-drift check: exact attention of at most kMaxDriftRows sampled
+// query rows per head, split over at most kMaxDriftSplits key ranges.
+constexpr int kMaxDriftRows = 128;
+constexpr int kMaxDriftSplits = 64;
+size_t drift_workspace_bytes(const Shape& s);
+hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K, const void* V, const void* O,
+                        const int32_t* rows, int n_rows, float* drift, void* ws, hipStream_t st);
+
 // PDDP grouping.  ws: int32 tmp [BH*Nq] followed by uint32 keys [BH*Nq].
 size_t pddp_workspace_bytes(const Shape& s);
 hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, void* ws, hipStream_t st);

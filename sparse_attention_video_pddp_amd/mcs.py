@@ -18,10 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libmcs.so")
 
 MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
 MCS_F32, MCS_BF16 = 0, 1
-MCS_WS_GROUP, MCS_WS_ANCHOR, MCS_WS_BLOCK = 0, 1, 2
+MCS_WS_GROUP, MCS_WS_ANCHOR, MCS_WS_BLOCK, MCS_WS_DRIFT = 0, 1, 2, 3
+MAX_DRIFT_ROWS = 128
 
 EXPORTED = ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
-            "mcs_block_select", "mcs_status_string", "mcs_last_error", "mcs_version")
+            "mcs_block_select", "mcs_residual_drift", "mcs_status_string", "mcs_last_error", "mcs_version")
 
 
 class Problem(ctypes.Structure):
@@ -69,8 +70,9 @@ def lib() -> ctypes.CDLL:
         L.mcs_anchor.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mcs_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mcs_block_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+        L.mcs_residual_drift.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, sz, vp]
         for f in ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
-                  "mcs_block_select"):
+                  "mcs_block_select", "mcs_residual_drift"):
             getattr(L, f).restype = ctypes.c_int
         L.mcs_status_string.argtypes = [ctypes.c_int]
         L.mcs_status_string.restype = ctypes.c_char_p
@@ -148,6 +150,14 @@ def block_select(p: Problem, Q, K, perm, idx, ws, ws_bytes: Optional[int] = None
                                   _stream(stream)))
 
 
+def residual_drift(p: Problem, Q, K, V, O, rows, drift, ws, n_rows: Optional[int] = None,
+                   ws_bytes: Optional[int] = None, stream=None) -> None:
+    n = rows.numel() if n_rows is None else n_rows
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().mcs_residual_drift(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(rows), n,
+                                    _ptr(drift), _ptr(ws), nbytes, _stream(stream)))
+
+
 class MCSparseAttention:
     """Per-layer state of the method across denoising steps: the groups
     (perm), selections (idx) and residual (R) of the last anchor, held in
@@ -200,3 +210,53 @@ class BlockSparseComparator:
         block_select(self.p, Q, K, self.perm, self.idx, self.ws, stream=stream)
         sparse_attn(self.p, Q, K, V, self.perm, self.idx, None, self.O, stream=stream)
         return self.O
+
+
+def drift_rows(Nq: int, n: int = MAX_DRIFT_ROWS):
+    """n query rows spread evenly over [0, Nq) (fewer if Nq < n), as a host list."""
+    n = max(1, min(n, Nq, MAX_DRIFT_ROWS))
+    return sorted({(2 * i + 1) * Nq // (2 * n) for i in range(n)})
+
+
+class AdaptiveAnchoring:
+    """Anchor schedule driven by the residual-drift check instead of a fixed
+    period: after every reuse step the drift of the sampled rows is measured
+    (mcs_residual_drift on the step's output), and the next step is an anchor
+    when the largest drift over the heads exceeds ``threshold`` or when
+    ``max_period`` steps have passed since the last anchor (0: no limit).
+    ``step(Q, K, V)`` returns O; ``history`` records (is_anchor, drift) per
+    step.  Reading the drift back costs one host synchronisation per reuse
+    step."""
+
+    def __init__(self, layer: MCSparseAttention, threshold: float, max_period: int = 0, n_rows: int = 64,
+                 device="cuda"):
+        import torch
+        self.layer, self.threshold, self.max_period = layer, threshold, max_period
+        p = layer.p
+        self.rows = torch.tensor(drift_rows(p.Nq, n_rows), dtype=torch.int32, device=device)
+        self.drift = torch.zeros((p.B, p.H), dtype=torch.float32, device=device)
+        b, _ = workspace_size(p, MCS_WS_DRIFT)
+        self.ws = torch.empty(max(b, 1), dtype=torch.uint8, device=device)
+        self.anchor_next = True
+        self.since = 0
+        self.history = []
+
+    @staticmethod
+    def decide(drift_max: float, threshold: float, since: int, max_period: int) -> bool:
+        """Whether the step after a reuse step with this drift is an anchor
+        (a NaN drift anchors too)."""
+        return not (drift_max <= threshold) or (max_period > 0 and since + 1 >= max_period)
+
+    def step(self, Q, K, V, stream=None):
+        if self.anchor_next or not self.layer.has_anchor:
+            O = self.layer.step(Q, K, V, True, stream=stream)
+            self.anchor_next, self.since = False, 0
+            self.history.append((True, None))
+            return O
+        O = self.layer.step(Q, K, V, False, stream=stream)
+        residual_drift(self.layer.p, Q, K, V, O, self.rows, self.drift, self.ws, stream=stream)
+        d = float(self.drift.max().item()) if self.drift.numel() else 0.0
+        self.since += 1
+        self.anchor_next = self.decide(d, self.threshold, self.since, self.max_period)
+        self.history.append((False, d))
+        return O

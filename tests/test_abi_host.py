@@ -133,3 +133,32 @@ def test_block_select_workspace_and_limits():
         mcs.block_select(base(Nkv=40000, k=32706, dtype="f32"), 16, 16, 32, 48, 64, ws_bytes=1 << 40, stream=0)
     assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
     mcs.block_select(base(Nq=0), None, None, None, None, None, ws_bytes=0, stream=0)
+
+
+def test_residual_drift_workspace_and_limits():
+    p = base()
+    b, bmin = mcs.workspace_size(p, mcs.MCS_WS_DRIFT)
+    assert b == bmin > 0
+    for n in (0, 129):
+        with pytest.raises(mcs.MCSError) as e:
+            mcs.residual_drift(p, 16, 16, 16, 16, 16, 32, 48, n_rows=n, ws_bytes=b, stream=0)
+        assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "n_rows" in str(e.value)
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.residual_drift(p, 16, 16, 16, 16, 16, 32, 48, n_rows=8, ws_bytes=b - 1, stream=0)
+    assert e.value.status == mcs.MCS_ERR_WORKSPACE
+    mcs.residual_drift(base(Nq=0), None, None, None, None, None, None, None, n_rows=8, ws_bytes=0, stream=0)
+
+
+def test_drift_rows_are_spread_and_bounded():
+    assert mcs.drift_rows(32760, 64)[0] >= 0 and mcs.drift_rows(32760, 64)[-1] < 32760
+    assert len(mcs.drift_rows(32760, 64)) == 64 and len(mcs.drift_rows(32760, 500)) == 128
+    assert mcs.drift_rows(5, 64) == [0, 1, 2, 3, 4]
+    r = mcs.drift_rows(1000, 10)
+    assert all(b - a == 100 for a, b in zip(r, r[1:]))
+
+
+def test_adaptive_schedule_decisions():
+    d = mcs.AdaptiveAnchoring.decide
+    assert not d(0.01, 0.02, 1, 0) and d(0.03, 0.02, 1, 0)
+    assert d(0.0, 0.02, 4, 5) and not d(0.0, 0.02, 3, 5)   # max_period counts steps since the anchor
+    assert d(float("nan"), 0.02, 1, 0)                     # a broken measurement anchors
