@@ -15,26 +15,25 @@
 // the unnormalised output relative to m); bf16 on MFMA with the per-wave core
 // of ring.hpp (4 waves x 32 rows, 64-key K/V tiles by direct-to-LDS copies),
 // float32 on the VALU (one wave per row and key range).  drift_combine_kernel:
-// per (head, 8-row block) the merged exact rows and their squared error and
-// norm against the caller's output; drift_final_kernel: per head, the sums in
-// block order and the ratio.
+// per (head, sampled row) the merged exact row and its squared error and norm
+// against the caller's output; drift_final_kernel: per head, the sums in row
+// order and the ratio.
 #include "mcs_kernels.hpp"
 #include "ring.hpp"
 
 namespace mcs {
 namespace {
 
-constexpr int kDriftTK = 64;     // keys per tile
-constexpr int kCombineRows = 8;  // sampled rows per combine workgroup
+constexpr int kDriftTK = 64;  // keys per tile
 
 struct DriftParams {
   const void *Q, *K, *V, *O;
   const int32_t* rows;
   float* pm;     // [BH][nsplit][kMaxDriftRows][2]: m (scaled log2), l
   float* po;     // [BH][nsplit][kMaxDriftRows][d]: unnormalised output
-  float* perr;   // [BH][nrb][2]: squared error, squared norm
+  float* perr;   // [BH][n_rows][2]: squared error, squared norm
   float* drift;  // [BH]
-  int Nq, Nkv, n_rows, nsplit, tps, nrb;
+  int Nq, Nkv, n_rows, nsplit, tps;
   float c;       // scale * log2(e)
   float scale;
   int causal_block, q_offset;
@@ -49,8 +48,8 @@ template <int D>
 __global__ __launch_bounds__(256) void rows_partial_bf16_kernel(DriftParams p) {
   constexpr int CH = D / 8, RPL = 64 / CH, LPW = kDriftTK / RPL / 4;  // DMA copies per wave per tile
   constexpr int BYTES = kDriftTK * D * 2;
-  __shared__ __attribute__((aligned(1024))) unsigned char ks[BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs[BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks[2][BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs[2][BYTES];
   const int bh = blockIdx.x / p.nsplit, sp = blockIdx.x - bh * p.nsplit;
   const int w = wave_id(), l = lane_id(), n = l & 31, h = l >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -78,19 +77,30 @@ __global__ __launch_bounds__(256) void rows_partial_bf16_kernel(DriftParams p) {
     const int rr = RPL * (wu + 4 * j) + l / CH;
     voff[j] = rr * (2 * D) + (((l % CH) ^ swz<D>(rr)) * 16);
   }
-  for (int t = t0; t < t1; ++t) {
-    // rows past the end of the head read as zeros (their keys are masked)
+  // rows past the end of the head read as zeros (their keys are masked)
+  auto issue = [&](int t, int slot) {
     const int bytes = (p.Nkv - t * kDriftTK) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Kh + (size_t)t * kDriftTK * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(Vh + (size_t)t * kDriftTK * D, bytes);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      dma16_buf(rk, voff[j], ks + (wu + 4 * j) * 1024);
-      dma16_buf(rv, voff[j], vs + (wu + 4 * j) * 1024);
+      dma16_buf(rk, voff[j], ks[slot] + (wu + 4 * j) * 1024);
+      dma16_buf(rv, voff[j], vs[slot] + (wu + 4 * j) * 1024);
     }
-    wait_vmcnt<0>();
+  };
+  // two-slot ring: tile t + 1 is copied while tile t is used; the slot it
+  // overwrites was last read before the previous iteration's final barrier
+  if (t0 < t1) issue(t0, 0);
+  for (int t = t0; t < t1; ++t) {
+    const int slot = (t - t0) & 1;
+    if (t + 1 < t1) {
+      issue(t + 1, slot ^ 1);
+      wait_vmcnt<2 * LPW>();  // tile t landed; t + 1 may still be in flight
+    } else {
+      wait_vmcnt<0>();
+    }
     __syncthreads();
-    fc.template blocks<2, 32 * 2 * D>(ks, vs, lim - t * kDriftTK, p.c);
+    fc.template blocks<2, 32 * 2 * D>(ks[slot], vs[slot], lim - t * kDriftTK, p.c);
     __syncthreads();
   }
   const float lt = half_sum(fc.l_run);
@@ -164,60 +174,74 @@ __global__ __launch_bounds__(64) void rows_partial_f32_kernel(DriftParams p) {
   }
 }
 
-// Merge the key ranges of kCombineRows sampled rows of one head and compare
-// with the caller's output rows.  Thread (row slot, channel).
+// Merge the key ranges of one sampled row of one head and compare with the
+// caller's output row.  Wave 0 takes one key range per lane (the maximum,
+// the weights 2^(m_s - M) and the merged sum, to LDS); then thread ch of the
+// first D merges that channel over the ranges, eight loads in flight.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void drift_combine_kernel(DriftParams p) {
-  constexpr int RP = 256 / D;  // rows per pass
-  __shared__ float red[2][256];
-  const int bh = blockIdx.x / p.nrb, rb = blockIdx.x - bh * p.nrb;
-  const int slot = threadIdx.x / D, ch = threadIdx.x - slot * D;
-  float e2 = 0.f, r2 = 0.f;
-  for (int rr = slot; rr < kCombineRows; rr += RP) {
-    const int r = rb * kCombineRows + rr;
-    if (r >= p.n_rows) break;
+  __shared__ float wgt[kMaxDriftSplits];
+  __shared__ float s_L;
+  __shared__ float red[2][D];
+  const int bh = blockIdx.x / p.n_rows, r = blockIdx.x - bh * p.n_rows;
+  const size_t base = (size_t)bh * p.nsplit * kMaxDriftRows + r;  // (bh, split 0, r)
+  const int tid = threadIdx.x;
+  if (tid < 64) {
     float M = -kInf;
-    for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.pm[2 * (((size_t)bh * p.nsplit + s) * kMaxDriftRows + r)]);
-    float L = 0.f, acc = 0.f;
-    if (M != -kInf) {
-      for (int s = 0; s < p.nsplit; ++s) {
-        const size_t pr = ((size_t)bh * p.nsplit + s) * kMaxDriftRows + r;
-        const float ms = p.pm[2 * pr];
-        if (ms == -kInf) continue;
-        const float wgt = exp2f(ms - M);
-        L = fmaf(p.pm[2 * pr + 1], wgt, L);
-        acc = fmaf(p.po[pr * D + ch], wgt, acc);
-      }
+    for (int s = tid; s < p.nsplit; s += 64) M = fmaxf(M, p.pm[2 * (base + (size_t)s * kMaxDriftRows)]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = 0.f;
+    for (int s = tid; s < p.nsplit; s += 64) {
+      const size_t pr = base + (size_t)s * kMaxDriftRows;
+      const float ms = p.pm[2 * pr];
+      const float wv = (ms == -kInf) ? 0.f : exp2f(ms - M);
+      wgt[s] = wv;
+      L = fmaf(p.pm[2 * pr + 1], wv, L);
     }
-    const float ex = L > 0.f ? acc / L : 0.f;
-    const float got = (float)((const T*)p.O)[((size_t)bh * p.Nq + sampled_row(p, r)) * D + ch];
-    const float dlt = got - ex;
-    e2 = fmaf(dlt, dlt, e2);
-    r2 = fmaf(ex, ex, r2);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (tid == 0) s_L = L;
   }
-  red[0][threadIdx.x] = e2;
-  red[1][threadIdx.x] = r2;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float a = 0.f, b = 0.f;
-    for (int i = 0; i < 256; ++i) {
-      a += red[0][i];
-      b += red[1][i];
+  if (tid < D) {
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < p.nsplit; ++s) acc = fmaf(p.po[(base + (size_t)s * kMaxDriftRows) * D + tid], wgt[s], acc);
+    const float L = s_L;
+    const float ex = L > 0.f ? acc / L : 0.f;
+    const float got = (float)((const T*)p.O)[((size_t)bh * p.Nq + sampled_row(p, r)) * D + tid];
+    const float dlt = got - ex;
+    red[0][tid] = dlt * dlt;
+    red[1][tid] = ex * ex;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float e2 = 0.f, r2 = 0.f;
+    for (int i = 0; i < D; ++i) {
+      e2 += red[0][i];
+      r2 += red[1][i];
     }
-    p.perr[2 * ((size_t)bh * p.nrb + rb)] = a;
-    p.perr[2 * ((size_t)bh * p.nrb + rb) + 1] = b;
+    p.perr[2 * ((size_t)bh * p.n_rows + r)] = e2;
+    p.perr[2 * ((size_t)bh * p.n_rows + r) + 1] = r2;
   }
 }
 
-__global__ __launch_bounds__(256) void drift_final_kernel(DriftParams p, int BH) {
-  const int bh = blockIdx.x * 256 + threadIdx.x;
-  if (bh >= BH) return;
+// One wave per head: lane i adds rows i, i + 64, ... in order, then a fixed
+// butterfly over the lanes.
+__global__ __launch_bounds__(64) void drift_final_kernel(DriftParams p) {
+  const int bh = blockIdx.x, l = threadIdx.x;
   float a = 0.f, b = 0.f;
-  for (int rb = 0; rb < p.nrb; ++rb) {
-    a += p.perr[2 * ((size_t)bh * p.nrb + rb)];
-    b += p.perr[2 * ((size_t)bh * p.nrb + rb) + 1];
+  for (int r = l; r < p.n_rows; r += 64) {
+    a += p.perr[2 * ((size_t)bh * p.n_rows + r)];
+    b += p.perr[2 * ((size_t)bh * p.n_rows + r) + 1];
   }
-  p.drift[bh] = b > 0.f ? sqrtf(a / b) : 0.f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    a += __shfl_xor(a, o, 64);
+    b += __shfl_xor(b, o, 64);
+  }
+  if (l == 0) p.drift[bh] = b > 0.f ? sqrtf(a / b) : 0.f;
 }
 
 void drift_split(const Shape& s, int& nsplit, int& tps) {
@@ -231,8 +255,7 @@ void drift_split(const Shape& s, int& nsplit, int& tps) {
 size_t drift_workspace_bytes(const Shape& s) {
   int nsplit, tps;
   drift_split(s, nsplit, tps);
-  const size_t nrb = (kMaxDriftRows + kCombineRows - 1) / kCombineRows;
-  return (size_t)s.BH * ((size_t)nsplit * kMaxDriftRows * (2 + s.d) + nrb * 2) * 4;
+  return (size_t)s.BH * ((size_t)nsplit * kMaxDriftRows * (2 + s.d) + kMaxDriftRows * 2) * 4;
 }
 
 hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K, const void* V, const void* O,
@@ -241,7 +264,6 @@ hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K,
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.rows = rows; p.drift = drift;
   p.Nq = s.Nq; p.Nkv = s.Nkv; p.n_rows = n_rows;
   drift_split(s, p.nsplit, p.tps);
-  p.nrb = (n_rows + kCombineRows - 1) / kCombineRows;
   p.pm = (float*)ws;
   p.po = p.pm + (size_t)s.BH * p.nsplit * kMaxDriftRows * 2;
   p.perr = p.po + (size_t)s.BH * p.nsplit * kMaxDriftRows * s.d;
@@ -256,12 +278,12 @@ hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K,
     if (s.d == 128) hipLaunchKernelGGL(rows_partial_f32_kernel<128>, g, dim3(64), 0, st, p);
     else hipLaunchKernelGGL(rows_partial_f32_kernel<64>, g, dim3(64), 0, st, p);
   }
-  const dim3 gcomb((unsigned)((long long)s.BH * p.nrb));
+  const dim3 gcomb((unsigned)((long long)s.BH * n_rows));
   if (bf16 && s.d == 128) hipLaunchKernelGGL((drift_combine_kernel<__bf16, 128>), gcomb, dim3(256), 0, st, p);
   else if (bf16) hipLaunchKernelGGL((drift_combine_kernel<__bf16, 64>), gcomb, dim3(256), 0, st, p);
   else if (s.d == 128) hipLaunchKernelGGL((drift_combine_kernel<float, 128>), gcomb, dim3(256), 0, st, p);
   else hipLaunchKernelGGL((drift_combine_kernel<float, 64>), gcomb, dim3(256), 0, st, p);
-  hipLaunchKernelGGL(drift_final_kernel, dim3((s.BH + 255) / 256), dim3(256), 0, st, p, s.BH);
+  hipLaunchKernelGGL(drift_final_kernel, dim3(s.BH), dim3(64), 0, st, p);
   return hipGetLastError();
 }
 
