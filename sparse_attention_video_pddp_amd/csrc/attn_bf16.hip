@@ -452,6 +452,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
     __syncthreads();
     if (ntiles > 0) reduce(ntiles - 1, (ntiles - 1) & 1);
   }
+  // keys of this range past the last visible tile: no query of the
+  // workgroup sees them, so their mass is 0 (every key of a row is written)
+  const int z0 = (t0 + ntiles) * 64, z1 = min((t0 + p.tps) * 64, p.Nkv);
+  for (int gl = 0; gl < GPW; ++gl) {
+    const int gg = u * GPW + gl;
+    if (gg >= p.c) break;
+    float* row = p.mass + ((size_t)bhl * p.c + gg) * p.Nkv;
+    for (int key = z0 + (int)threadIdx.x; key < z1; key += 64 * NW) row[key] = 0.f;
+  }
 }
 
 template <typename P>

@@ -26,6 +26,10 @@ SMALL = {
     "large_small": synth.get("large").with_(name="large_small", H=2, grid=(4, 15, 20), keep_permille=300),
     # 3D-local field generator, d=64, G=128: 2048 tokens -> 16 groups, k=205
     "stress_small": synth.get("stress").with_(name="stress_small", H=2, grid=(8, 16, 16), keep_permille=100),
+    # query chunk in the middle of the video: the last two frames are visible to no query, so
+    # their keys must get mass 0 (not whatever the workspace held) and never be selected
+    "causal_mid": synth.get("causal").with_(name="causal_mid", H=2, grid=(6, 10, 15), q_frames=(2, 4),
+                                            causal_block=150, keep_permille=100),
     # batch of two videos (B=2, H=2): every (b, h) has its own grouping, selection and residual
     "batch_small": synth.get("bidir5").with_(name="batch_small", B=2, H=2, grid=(2, 12, 20), keep_permille=150),
     # fp32 path with B=2
