@@ -260,3 +260,69 @@ class AdaptiveAnchoring:
         self.anchor_next = self.decide(d, self.threshold, self.since, self.max_period)
         self.history.append((False, d))
         return O
+
+
+class ChunkedCausalStream:
+    """Chunked autoregressive generation over a K/V cache: the video is made
+    chunk by chunk (``frames_per_chunk`` frames of ``frame_tokens`` tokens),
+    each chunk denoised over several steps while it attends, frame-block
+    causally, to the finished chunks and to itself.
+
+    The cache holds the K and V rows of the whole video, [B,H,capacity,d],
+    zero where nothing has been generated yet; chunk c's queries sit at
+    positions c*chunk_tokens.. of it.  Every chunk is an ordinary problem with
+    Nkv = capacity, q_offset = c*chunk_tokens and causal_block = frame_tokens:
+    keys past the chunk's last frame are invisible, so neither the cache's
+    unwritten rows nor its size change any result (they must only be finite,
+    hence the zeros).  Grouping, selections and residual are per chunk (a
+    fresh ``MCSparseAttention`` in ``begin_chunk``); the anchor schedule inside
+    a chunk is the caller's.  ``step`` writes the chunk's current K/V rows
+    into the cache (or the caller fills ``kv_rows()`` in place) and runs the
+    step."""
+
+    def __init__(self, B: int, H: int, d: int, frame_tokens: int, frames_per_chunk: int, n_chunks: int,
+                 group_size: int, k: int, scale: Optional[float] = None, dtype: str = "bf16",
+                 pddp_iters: int = 32, device="cuda"):
+        import torch
+        self.B, self.H, self.d = B, H, d
+        self.frame_tokens = frame_tokens
+        self.chunk_tokens = frame_tokens * frames_per_chunk
+        self.n_chunks = n_chunks
+        self.capacity = self.chunk_tokens * n_chunks
+        self.G, self.k, self.scale, self.dtype, self.iters = group_size, k, scale, dtype, pddp_iters
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.K = torch.zeros((B, H, self.capacity, d), dtype=dt, device=device)
+        self.V = torch.zeros_like(self.K)
+        self.device = device
+        self.chunk = -1
+        self.layer: Optional[MCSparseAttention] = None
+
+    def problem(self, c: int) -> Problem:
+        return problem(self.B, self.H, self.chunk_tokens, self.capacity, self.d, self.G, self.k, self.scale,
+                       causal_block=self.frame_tokens, q_offset=c * self.chunk_tokens, pddp_iters=self.iters,
+                       dtype=self.dtype)
+
+    def rows(self, c: Optional[int] = None) -> slice:
+        c = self.chunk if c is None else c
+        return slice(c * self.chunk_tokens, (c + 1) * self.chunk_tokens)
+
+    def begin_chunk(self) -> Problem:
+        if self.chunk + 1 >= self.n_chunks:
+            raise RuntimeError("the stream's capacity is used up")
+        self.chunk += 1
+        self.layer = MCSparseAttention(self.problem(self.chunk), device=self.device)
+        return self.layer.p
+
+    def kv_rows(self):
+        """Views of the current chunk's K and V rows in the cache."""
+        r = self.rows()
+        return self.K[:, :, r], self.V[:, :, r]
+
+    def step(self, Q, K_chunk=None, V_chunk=None, is_anchor: bool = False, stream=None):
+        if self.layer is None:
+            raise RuntimeError("begin_chunk() first")
+        if K_chunk is not None:
+            k, v = self.kv_rows()
+            k.copy_(K_chunk)
+            v.copy_(V_chunk)
+        return self.layer.step(Q, self.K, self.V, is_anchor, stream=stream)
