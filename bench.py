@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
                     help="derive per-launch HBM traffic from FETCH_SIZE/WRITE_SIZE counter CSVs of --config, "
                          "update profiles/traffic.json and exit")
+    ap.add_argument("--stream", action="store_true",
+                    help="instead of the metric: chunked-causal streaming of the frame-causal workload's whole "
+                         "video (chunks of its query-chunk length, each an anchor and reuse steps over the "
+                         "K/V cache); prints one JSON line of per-chunk times")
     ap.add_argument("--title", default="", help="title for --summarize-trace")
     ap.add_argument("--note", default="", help="paragraph for --summarize-trace")
     return ap.parse_args()
@@ -276,6 +280,82 @@ def cpu_baseline(w, host0, host1, nheads: int, reuse_budget_s: float = 10.0):
             "cpu": platform.processor() or platform.machine(), "numpy": np.__version__}
 
 
+def stream_main(args) -> None:
+    """Chunked-causal streaming at full size: the frame-causal workload's video
+    (grid T x H x W, chunks of its query-chunk length) generated chunk by chunk
+    over a zero-initialised K/V cache of the whole video.  Inputs: the
+    workload's generator for the whole video at step 0 (queries of every
+    frame), then per step an extra drift of the current chunk's rows drawn on
+    the device (seeded).  Timed with HIP events per call, caches flushed."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs, synth
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+
+    base = synth.get("causal")
+    T, Hg, Wg = base.grid
+    fpc = base.q_frames[1] - base.q_frames[0]
+    full = base.with_(name="causal_video", q_frames=(0, T))
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    (Qa, Ka, Va), _ = device_inputs(full, 0)
+    ft = Hg * Wg
+    n_chunks = T // fpc
+    st = mcs.ChunkedCausalStream(full.B, full.H, full.d, ft, fpc, n_chunks, full.group_size, full.k, full.scale,
+                                 full.dtype, full.pddp_iters)
+    A = base.anchor_every
+    steps = max(A, 4)
+    # untimed: one anchor and one reuse step of a first chunk (first launches of every kernel)
+    warm = mcs.ChunkedCausalStream(full.B, full.H, full.d, ft, fpc, n_chunks, full.group_size, full.k,
+                                   full.scale, full.dtype, full.pddp_iters)
+    warm.begin_chunk()
+    wr = warm.rows()
+    for anchor in (True, False):
+        warm.step(Qa[:, :, wr], Ka[:, :, wr], Va[:, :, wr], anchor)
+    torch.cuda.synchronize()
+    del warm
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    rec = []
+    for c in range(n_chunks):
+        st.begin_chunk()
+        r = st.rows()
+        Q, K, V = Qa[:, :, r].clone(), Ka[:, :, r].clone(), Va[:, :, r].clone()
+        for s in range(steps):
+            if s:
+                for X in (Q, K, V):
+                    X += (full.drift * torch.randn(X.shape, generator=gen, device=dev)).to(X.dtype)
+            anchor = s % A == 0
+            scratch.fill_(s & 255)
+            a, b = ev(), ev()
+            a.record(stream)
+            st.step(Q, K, V, anchor, stream=stream)
+            b.record(stream)
+            rec.append((c, anchor, a, b))
+    torch.cuda.synchronize()
+    per = {}
+    for c, anchor, a, b in rec:
+        per.setdefault(c, {"anchor_ms": [], "reuse_ms": []})["anchor_ms" if anchor else "reuse_ms"].append(
+            a.elapsed_time(b))
+    chunks = [{"chunk": c, "visible_keys": (c + 1) * st.chunk_tokens,
+               "anchor_ms": round(statistics.fmean(v["anchor_ms"]), 4),
+               "reuse_ms": round(statistics.fmean(v["reuse_ms"]), 4)} for c, v in sorted(per.items())]
+    total = sum(a.elapsed_time(b) for _, _, a, b in rec)
+    out = {"metric": "chunked-causal streaming: ms per chunk (group + anchor + reuse steps)",
+           "value": round(total / n_chunks, 4), "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+           "dtype": full.dtype, "data": "synthetic",
+           "config": {"workload": f"frame-causal video {T}x{Hg}x{Wg} = {T * ft} tokens, B={full.B}, H={full.H}, "
+                                  f"d={full.d}, chunks of {fpc} frames ({st.chunk_tokens} queries), K/V cache "
+                                  f"of {st.capacity} rows, groups of {full.group_size}, k={full.k}, {steps} steps "
+                                  f"per chunk, anchor every {A}",
+                      "chunks": n_chunks, "steps_per_chunk": steps},
+           "chunks": chunks, "cache": "flushed (512 MB overwrite before every timed call)",
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -289,6 +369,9 @@ def main():
         print("bench.py measures one GPU only: every box here has one MI355X and the method's "
               "kernels run on one GPU's share; --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
+    if args.stream:
+        stream_main(args)
+        return
     import numpy as np
     import torch
     from sparse_attention_video_pddp_amd import mcs, synth
