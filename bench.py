@@ -100,16 +100,38 @@ def load_traffic(kernel: str, config: str):
 
 def _short_kernel(name: str) -> str:
     import re
+    m = re.match(r"_ZN3mcs12_GLOBAL__N_1(\d+)", name)
+    if m:  # names the profiler leaves mangled (a __bf16 template argument): name<args>
+        n = int(m.group(1))
+        rest = name[m.end():]
+        ident, rest = rest[:n], rest[n:]
+        pretty = []
+        for a in re.finditer(r"DF16b|Li(\d+)E|(?<=I)f|(?<=E)f", rest.split("EEv")[0]):
+            pretty.append("__bf16" if a.group(0) == "DF16b" else (a.group(1) if a.group(1) else "float"))
+        return ident + (f"<{', '.join(pretty)}>" if pretty else "")
     name = name.replace("void ", "").replace("mcs::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)
 
 
+def launch_label(kernel: str, prev: str) -> str:
+    """Row of a launch in the profile summaries.  The gathered-attention
+    kernel serves three calls: right after a top-k launch it is the anchor's
+    epilogue (it forms R), right after a block selection it is the
+    block-sparse comparator, otherwise the reuse step (the metric)."""
+    if kernel.startswith("sparse_ring_kernel"):
+        if prev.startswith("topk_kernel"):
+            return kernel + " (anchor epilogue)"
+        if prev.startswith("block_select"):
+            return kernel + " (block-sparse comparator)"
+    return kernel
+
+
 def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
     """Markdown table of per-kernel durations from a rocprofv3 kernel-trace
-    database (its `kernels` view, read with sqlite3).  Reuse-kernel launches
-    that directly follow a top-k launch are the anchor's epilogue (they form
-    R); they get a row of their own so that the reuse row is comparable with
-    the live timing of mcs_sparse_attn."""
+    database (its `kernels` view, read with sqlite3).  Launches of the
+    gathered-attention kernel for the anchor's epilogue and for the
+    block-sparse comparator get rows of their own (launch_label), so that the
+    reuse row is comparable with the live timing of mcs_sparse_attn."""
     import sqlite3
     con = sqlite3.connect(os.path.abspath(db))
     rows = con.execute("select name, start, end from kernels order by start").fetchall()
@@ -117,8 +139,7 @@ def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
     stats, prev = {}, ""
     for name, t0, t1 in rows:
         k = _short_kernel(name)
-        key = k + " (anchor epilogue)" if k.startswith("sparse_ring_kernel") and prev.startswith("topk_kernel") else k
-        stats.setdefault(key, []).append((t1 - t0) / 1e3)
+        stats.setdefault(launch_label(k, prev), []).append((t1 - t0) / 1e3)
         prev = k
     total = sum(sum(v) for v in stats.values())
     with open(out, "w") as f:
@@ -137,9 +158,10 @@ def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
 def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: str, cmd_write: str) -> None:
     """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB
-    device copy of the same run.  Reuse-kernel launches that directly follow
-    a top-k launch are anchor epilogues (they update R instead of writing O)
-    and are left out.  Writes profiles/traffic.json and a markdown summary."""
+    device copy of the same run.  Launches of the gathered-attention kernel
+    for the anchor's epilogue and for the block-sparse comparator are kept
+    apart (launch_label); traffic.json holds the reuse launches.  Writes
+    profiles/traffic.json and a markdown summary."""
     import csv
     per = {}
     for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -149,16 +171,21 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
             if r["Counter_Name"] != tag:
                 continue
             k = _short_kernel(r["Kernel_Name"])
-            if not (k.startswith("sparse_ring_kernel") and prev.startswith("topk_kernel")):
-                vals.setdefault(k, []).append(float(r["Counter_Value"]))
+            vals.setdefault(launch_label(k, prev), []).append(float(r["Counter_Value"]))
             prev = k
         per[tag] = vals
     copy = [k for k in per["FETCH_SIZE"] if "copyBuffer" in k]
     if not copy:
         raise SystemExit("no device copy in the counter runs (run bench.py with --copy-calibration)")
     gib_kib = float(1 << 20)
-    f_fac = gib_kib / statistics.fmean(per["FETCH_SIZE"][copy[0]])
-    w_fac = gib_kib / statistics.fmean(per["WRITE_SIZE"][copy[0]])
+
+    def copy_reading(tag):
+        # median over the 1 GiB copies (other, small device copies share the kernel name)
+        v = per[tag][copy[0]]
+        return statistics.median(x for x in v if x > 0.25 * max(v))
+
+    f_read, w_read = copy_reading("FETCH_SIZE"), copy_reading("WRITE_SIZE")
+    f_fac, w_fac = gib_kib / f_read, gib_kib / w_read
     try:
         with open(TRAFFIC_FILE) as fh:
             table = json.load(fh)
@@ -167,10 +194,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
     lines = [f"# HBM traffic per launch, {config}\n",
              "Two counter runs of the same command (repository root, one MI355X):\n",
              f"```\n{cmd_fetch}\n{cmd_write}\n```\n",
-             f"Calibration: the 1 GiB device copy in the same runs reads FETCH_SIZE = "
-             f"{statistics.fmean(per['FETCH_SIZE'][copy[0]]):.0f} KiB and WRITE_SIZE = "
-             f"{statistics.fmean(per['WRITE_SIZE'][copy[0]]):.0f} KiB, so fetch counts are scaled by "
-             f"{f_fac:.3f} and write counts by {w_fac:.3f}.\n",
+             f"Calibration: the 1 GiB device copies in the same runs read FETCH_SIZE = "
+             f"{f_read:.0f} KiB and WRITE_SIZE = {w_read:.0f} KiB (median per copy), so fetch counts are "
+             f"scaled by {f_fac:.3f} and write counts by {w_fac:.3f}.\n",
              "| kernel | launches | fetch (MB/launch) | write (MB/launch) | total (MB/launch) |",
              "|---|---:|---:|---:|---:|"]
     for k in sorted(per["FETCH_SIZE"]):
@@ -181,7 +207,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
         lines.append(f"| `{k}` | {len(per['FETCH_SIZE'][k])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
                      f"{(fb + wb) / 1e6:.1f} |")
         base = k.split("<")[0]
-        if base in KERNEL_SOURCES:
+        if base in KERNEL_SOURCES and "(" not in k:
             table.setdefault(base, {})[config] = {
                 "bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                 "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
