@@ -34,6 +34,13 @@ SMALL = {
     "batch_small": synth.get("bidir5").with_(name="batch_small", B=2, H=2, grid=(2, 12, 20), keep_permille=150),
     # fp32 path with B=2
     "tiny_batch": synth.get("tiny").with_(name="tiny_batch", B=2, H=1, grid=(2, 16, 16)),
+    # bf16, d=64 with groups of 64 (the stress workload has G=128): 960 tokens -> 15 groups, k=144
+    "d64_g64": synth.get("bidir5").with_(name="d64_g64", H=2, d=64, grid=(4, 12, 20), keep_permille=150,
+                                         scale=1.0 / 8.0),
+    # fp32, d=128 with groups of 128, frame-causal: 900 queries of 1200 keys, k=120
+    "f32_d128_g128": synth.get("tiny").with_(name="f32_d128_g128", H=2, d=128, group_size=128,
+                                             grid=(8, 10, 15), q_frames=(2, 8), causal_block=150,
+                                             keep_permille=100, scale=1.0 / 128 ** 0.5),
 }
 
 
