@@ -16,8 +16,9 @@
 // selected ahead of a real key (at most n are selected) and every stripe can
 // be processed without lane masks; only the final emit skips them.
 //
-// Threshold: three MSB-first radix passes (12, 12 and 8 bits) over the
-// elements whose key matches the digits found so far; histograms in LDS.
+// Threshold: three MSB-first radix passes (12, 12 and 8 bits, or 12, 12 and
+// HI-24 bits for keys below 2^HI) over the elements whose key matches the
+// digits found so far; histograms in LDS.
 // The result is the need-th largest key T and how many keys equal to T are
 // selected.
 //
@@ -112,9 +113,12 @@ struct BlockSelect {
   }
 
   // T = need-th largest key (1 <= need <= n); tie_need = how many keys equal
-  // to T belong to the selection.
-  template <class Keys>
+  // to T belong to the selection.  HI: keys are below 2^HI (31 for the bit
+  // patterns of non-negative floats), so the first pass takes bits
+  // [HI-12, HI) and the last the HI-24 lowest bits.
+  template <int HI = 32, class Keys>
   __device__ void threshold(const Keys& keys, int need, Shared& sh, uint32_t& T, int& tie_need) const {
+    static_assert(HI >= 25 && HI <= 32, "three passes of at most 12 bits");
     const int t = threadIdx.x;
     const int top = NBIN - 1 - t * BPT;  // this thread's bins: top, top-1, ..., top-BPT+1
 #pragma unroll
@@ -125,8 +129,8 @@ struct BlockSelect {
     int krem = need;  // rank, from the top, still to locate among keys matching prefix
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-      const uint32_t dmask = pass == 2 ? 0xFFu : 0xFFFu;
+      const int shift = pass == 0 ? HI - 12 : (pass == 1 ? HI - 24 : 0);
+      const uint32_t dmask = pass == 2 ? (1u << (HI - 24)) - 1u : 0xFFFu;
       stripes(0, nstripes, keys, [&](int, int, uint32_t u) {
         const bool m = (u & pmask) == prefix;
         if (__ballot(m)) {  // later passes: most stripes hold no matching key
