@@ -63,6 +63,9 @@ def parse():
                     help="instead of the metric: chunked-causal streaming of the frame-causal workload's whole "
                          "video (chunks of its query-chunk length, each an anchor and reuse steps over the "
                          "K/V cache); prints one JSON line of per-chunk times")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="OUT_MD then pairs CSV CMD of rocprofv3 derived-counter runs (MfmaUtil, MfmaFlopsBF16, "
+                         "LdsUtil, LdsBankConflict, VALUBusy): write a per-kernel markdown table and exit")
     ap.add_argument("--title", default="", help="title for --summarize-trace")
     ap.add_argument("--note", default="", help="paragraph for --summarize-trace")
     return ap.parse_args()
@@ -217,6 +220,46 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
     out = os.path.join(ROOT, "profiles", f"traffic_{config}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
+    print(open(out).read())
+
+
+def summarize_pmc(out: str, runs, title: str, note: str) -> None:
+    """Per-kernel means of rocprofv3 derived counters (one row per kernel
+    label, launch_label), from one or more counter runs; MFMA TFLOP/s from
+    MfmaFlopsBF16 over each dispatch's own duration (counter runs serialise
+    the dispatches)."""
+    import csv
+    vals = {}
+    for path, _ in runs:
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: (int(r["Dispatch_Id"]), r["Counter_Name"]))
+        prev, last_id = "", None
+        for r in rows:
+            k = _short_kernel(r["Kernel_Name"])
+            if r["Dispatch_Id"] != last_id:
+                label = launch_label(k, prev)
+                prev, last_id = k, r["Dispatch_Id"]
+            d = vals.setdefault(label, {})
+            v = float(r["Counter_Value"])
+            d.setdefault(r["Counter_Name"], []).append(v)
+            if r["Counter_Name"] == "MfmaFlopsBF16":
+                dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                d.setdefault("tflops", []).append(v / dt / 1e12 if dt > 0 else 0.0)
+    cols = [("MfmaUtil", "MFMA busy %", 1), ("tflops", "MFMA TFLOP/s", 1), ("LdsUtil", "LDS busy %", 1),
+            ("LdsBankConflict", "bank-conflict cycles per LDS cycle", 3), ("VALUBusy", "VALU busy %", 1)]
+    with open(out, "w") as f:
+        f.write(f"# {title}\n\nCommands (repository root, one MI355X; one run per counter set):\n\n```\n")
+        for _, cmd in runs:
+            f.write(cmd + "\n")
+        f.write("```\n\n")
+        if note:
+            f.write(note + "\n\n")
+        f.write("| kernel | launches | " + " | ".join(c[1] for c in cols) + " |\n|---|---:|" +
+                "---:|" * len(cols) + "\n")
+        for k in sorted(vals, key=lambda k: -statistics.fmean(vals[k].get("MfmaUtil", [0.0]))):
+            d = vals[k]
+            n = max(len(v) for v in d.values())
+            cells = [f"{statistics.fmean(d[c]):.{nd}f}" if c in d else "" for c, _, nd in cols]
+            f.write(f"| `{k}` | {n} | " + " | ".join(cells) + " |\n")
     print(open(out).read())
 
 
@@ -387,6 +430,12 @@ def main():
     if args.summarize_trace:
         db, out, cmd = args.summarize_trace
         summarize_trace(db, out, args.title or f"Kernel trace, {args.config}", cmd, args.note)
+        return
+    if args.summarize_pmc:
+        a = args.summarize_pmc
+        if len(a) < 3 or len(a) % 2 == 0:
+            raise SystemExit("--summarize-pmc OUT_MD CSV CMD [CSV CMD ...]")
+        summarize_pmc(a[0], list(zip(a[1::2], a[2::2])), args.title or "Counters", args.note)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters[:2], args.config, *args.summarize_counters[2:])

@@ -63,10 +63,18 @@ struct BlockSelect {
   static constexpr int VB = 64;         // stripes per split block (one per lane; VB * NW <= NT)
   static_assert(VPT >= 0, "register cache");
 
+  // LDS layouts padded against bank conflicts: histogram bin b at
+  // b + b / BPT (the BPT bins a thread scans are consecutive, so lanes land
+  // BPT + 1 words apart, an odd stride); split entry e = (stripe slot l,
+  // wave w) = l * NW + w at e + e / NW (written by lane l of wave w: stride
+  // NW + 1).
+  static __device__ __forceinline__ int hidx(int b) { return b + b / BPT; }
+  static __device__ __forceinline__ int eidx(int e) { return e + e / NW; }
+
   struct Shared {
-    int hist[NBIN];
-    int cnt_gt[NT];
-    int cnt_eq[NT];
+    int hist[NBIN + NBIN / BPT];
+    int cnt_gt[VB * (NW + 1)];
+    int cnt_eq[VB * (NW + 1)];
     int wsum[NW];
     uint32_t prefix;
     int krem;
@@ -122,7 +130,7 @@ struct BlockSelect {
     const int t = threadIdx.x;
     const int top = NBIN - 1 - t * BPT;  // this thread's bins: top, top-1, ..., top-BPT+1
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) sh.hist[top - b] = 0;
+    for (int b = 0; b < BPT; ++b) sh.hist[hidx(top - b)] = 0;
     __syncthreads();
     const int nstripes = VPT > 0 ? VPT : (n + NT - 1) / NT;
     uint32_t prefix = 0, pmask = 0;
@@ -134,14 +142,14 @@ struct BlockSelect {
       stripes(0, nstripes, keys, [&](int, int, uint32_t u) {
         const bool m = (u & pmask) == prefix;
         if (__ballot(m)) {  // later passes: most stripes hold no matching key
-          if (m) atomicAdd(&sh.hist[(u >> shift) & dmask], 1);
+          if (m) atomicAdd(&sh.hist[hidx((u >> shift) & dmask)], 1);
         }
       });
       __syncthreads();
       int cnt[BPT], local = 0;
 #pragma unroll
       for (int b = 0; b < BPT; ++b) {
-        cnt[b] = sh.hist[top - b];
+        cnt[b] = sh.hist[hidx(top - b)];
         local += cnt[b];
       }
       int total;
@@ -159,7 +167,7 @@ struct BlockSelect {
         }
       }
 #pragma unroll
-      for (int b = 0; b < BPT; ++b) sh.hist[top - b] = 0;
+      for (int b = 0; b < BPT; ++b) sh.hist[hidx(top - b)] = 0;
       __syncthreads();
       prefix = sh.prefix;
       krem = sh.krem;
@@ -191,24 +199,24 @@ struct BlockSelect {
         my_eq = (l == s - s0) ? eqc : my_eq;
       });
       if (l < s1 - s0) {
-        sh.cnt_gt[l * NW + w] = my_gt;
-        sh.cnt_eq[l * NW + w] = my_eq;
+        sh.cnt_gt[eidx(l * NW + w)] = my_gt;
+        sh.cnt_eq[eidx(l * NW + w)] = my_eq;
       }
       __syncthreads();
       const int e = threadIdx.x;  // entry (stripe s0 + e / NW, wave e % NW), in index order
       const bool ein = e < (s1 - s0) * NW;
-      const int eqc = ein ? sh.cnt_eq[e] : 0, gtc = ein ? sh.cnt_gt[e] : 0;
+      const int eqc = ein ? sh.cnt_eq[eidx(e)] : 0, gtc = ein ? sh.cnt_gt[eidx(e)] : 0;
       int eq_tot, sel_tot;
       const int eq_off = base_eq + block_excl_scan<NT>(eqc, sh.wsum, eq_tot);
       const int selc = gtc + min(max(tie_need - eq_off, 0), eqc);
       const int sel_off = base_sel + block_excl_scan<NT>(selc, sh.wsum, sel_tot);
       if (ein) {
-        sh.cnt_eq[e] = eq_off;
-        sh.cnt_gt[e] = sel_off;
+        sh.cnt_eq[eidx(e)] = eq_off;
+        sh.cnt_gt[eidx(e)] = sel_off;
       }
       __syncthreads();
-      const int my_eo = l < s1 - s0 ? sh.cnt_eq[l * NW + w] : 0;
-      const int my_so = l < s1 - s0 ? sh.cnt_gt[l * NW + w] : 0;
+      const int my_eo = l < s1 - s0 ? sh.cnt_eq[eidx(l * NW + w)] : 0;
+      const int my_so = l < s1 - s0 ? sh.cnt_gt[eidx(l * NW + w)] : 0;
       stripes(s0, s1, keys, [&](int s, int j, uint32_t u) {
         bool sel = u > T;
         const uint64_t eqm = __ballot(u == T);
