@@ -9,9 +9,9 @@
 // lowest index first.  The patterns of non-negative floats are below 2^31, so
 // the first radix pass takes bits 30..19 (8 exponent and 4 mantissa bits):
 // twice the bins of a pass over bits 31..20, half the atomic contention on
-// rows whose masses share few octaves (bidir5: 514 -> 440 us per call).  Rows of up to 81920 keys are held in registers (up to
-// 64 keys per thread of a 512-thread workgroup, or 80 of a 1024-thread one;
-// one HBM read); longer rows are re-read on each pass.
+// rows whose masses share few octaves.  Rows of up to 81920 keys are held in
+// registers (up to 64 keys per thread of a 512-thread workgroup, or 80 of a
+// 1024-thread one; one HBM read); longer rows are re-read on each pass.
 #include "mcs_kernels.hpp"
 #include "select.hpp"
 
