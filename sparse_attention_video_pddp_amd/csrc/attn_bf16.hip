@@ -195,11 +195,11 @@ __device__ __forceinline__ void store_row_f32(float* dst, const Flash<D>& st, fl
 }
 
 // ---------------------------------------------------------------------------
-// Dense attention, natural token order: 256 queries (8 waves) per workgroup
-// at d = 128, two waves per SIMD (230 registers), so one staged K/V tile
-// serves eight waves (6.80 -> 6.39 ms at 32760 tokens, 12 heads against four
-// waves); 128 queries (4 waves) at d = 64, three waves per SIMD.  Two LDS
-// tiles, one barrier per tile.
+// Dense attention, natural token order: 256 queries (8 waves) per workgroup,
+// so one staged K/V tile serves eight waves (against four: 6.80 -> 6.39 ms at
+// 32760 tokens, 12 heads, d = 128; 84.3 -> 80.1 ms at 131072 tokens, 16
+// heads, d = 64).  Two waves per SIMD at d = 128 (230 registers), four at
+// d = 64 (123).  Two LDS tiles, one barrier per tile.
 // ---------------------------------------------------------------------------
 struct DenseParams {
   const __bf16 *Q, *K, *V;
@@ -212,7 +212,7 @@ struct DenseParams {
 };
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2))) void dense_bf16_kernel(DenseParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void dense_bf16_kernel(DenseParams p) {
   constexpr int NT = 64 * NW, QR = 32 * NW;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][64 * Tile<D>::KS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2][64 * Tile<D>::VS];
@@ -480,13 +480,13 @@ hipError_t launch_dense_bf16(const Shape& s, const void* Q, const void* K, const
   DenseParams p;
   p.Q = (const __bf16*)Q; p.K = (const __bf16*)K; p.V = (const __bf16*)V; p.O = (__bf16*)O;
   p.lse = lse; p.Ofull = Ofull;
-  const int qr = s.d == 128 ? 256 : 128;
+  const int qr = 256;  // 8 waves x 32 queries
   p.Nq = s.Nq; p.Nkv = s.Nkv; p.n_qtiles = (s.Nq + qr - 1) / qr;
   p.c = s.scale * kLog2e; p.causal_block = s.causal_block; p.q_offset = s.q_offset;
   dim3 grid;
   grid_for(p, s.BH * p.n_qtiles, grid);
   if (s.d == 128) hipLaunchKernelGGL((dense_bf16_kernel<128, 8>), grid, dim3(512), 0, st, p);
-  else hipLaunchKernelGGL((dense_bf16_kernel<64, 4>), grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((dense_bf16_kernel<64, 8>), grid, dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
