@@ -72,3 +72,41 @@ def test_attention_over_a_foreign_cache(cuda):
         for r in reps:
             log(f"  cache attention head {h}: {r}")
         assert_reports(reps, f"cache attention head {h}")
+
+
+def test_largest_kept_key_count(cuda):
+    """The largest supported selection: k = 28672 kept keys per group (the
+    bf16 path's on-chip index table is full) out of a 30240-key cache
+    (472.5 key tiles: a ragged tail), two groups of 64 queries.  The boundary
+    of the top-k then lies deep in the low-mass tail, where near-ties are
+    common; tests/parity.py validates the GPU's choice there."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import _to_tensor
+    from tests.gpu_runner import log
+    wq = WQ.with_(name="maxk_q", H=1, grid=(1, 8, 16))
+    wkv = wq.with_(name="maxk_kv", cfg_id=98, grid=(12, 40, 63))
+    k = 28672
+    assert wkv.Nkv == 30240 and wq.Nq == 128
+    p = mcs.problem(1, 1, wq.Nq, wkv.Nkv, wq.d, wq.group_size, k, wq.scale, dtype=wq.dtype,
+                    pddp_iters=wq.pddp_iters)
+    q0 = synth.head_inputs(wq, 0, 0, 0)[0]
+    q1 = synth.head_inputs(wq, 0, 0, 1)[0]
+    _, kk, vv = synth.head_inputs(wkv, 0, 0, 0)
+    dev = lambda x: _to_tensor(x, wq.dtype)[None, None].to("cuda")  # noqa: E731
+    Q0, Q1, K, V = dev(q0), dev(q1), dev(kk), dev(vv)
+    st = mcs.MCSparseAttention(p)
+    O0 = st.step(Q0, K, V, True).clone()
+    O1 = st.step(Q1, K, V, False).clone()
+    torch.cuda.synchronize()
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    kd, vd = f64(kk), f64(vv)
+    case = HeadCase(f64(q0), kd, vd, f64(q1), kd, vd,
+                    perm=st.perm[0, 0].cpu().numpy(), idx=st.idx[0, 0].cpu().numpy(),
+                    O_full=O0[0, 0].float().cpu().numpy().astype(np.float64),
+                    R=st.R[0, 0].float().cpu().numpy().astype(np.float64),
+                    O_reuse=O1[0, 0].float().cpu().numpy().astype(np.float64))
+    reps = check_head(case, wq.group_size, k, wq.scale, 0, 0, wq.pddp_iters)
+    for r in reps:
+        log(f"  k = {k} of {wkv.Nkv}: {r}")
+    assert_reports(reps, f"k = {k}")
