@@ -116,25 +116,38 @@ def _short_kernel(name: str) -> str:
     return re.sub(r"\(.*$", "", name)
 
 
+FLUSH_KERNEL = "FillFunctor<unsigned char>"   # the 512 MB cache-flush fill before every timed call
+
+
 def launch_label(kernel: str, prev: str) -> str:
-    """Row of a launch in the profile summaries.  The gathered-attention
-    kernel serves three calls: right after a top-k launch it is the anchor's
-    epilogue (it forms R), right after a block selection it is the
-    block-sparse comparator, otherwise the reuse step (the metric)."""
+    """Row of a launch in the profile summaries, from the kernel launched just
+    before it.  Every timed call of the bench starts right after the cache
+    flush, so a launch right after the flush fill is a timed (cold) call and
+    keeps the plain kernel name: those rows are comparable with the live
+    HIP-event timings.  The gathered-attention kernel otherwise is the anchor's
+    epilogue (after a top-k launch: it forms R), the block-sparse comparator
+    (after a block selection) or an untimed call (warm-cache or fidelity
+    pass); the dense kernel after a PDDP launch is the anchor's exact pass,
+    else an untimed call."""
+    cold = FLUSH_KERNEL in prev
     if kernel.startswith("sparse_ring_kernel"):
         if prev.startswith("topk_kernel"):
             return kernel + " (anchor epilogue)"
         if prev.startswith("block_select"):
             return kernel + " (block-sparse comparator)"
+        return kernel if cold else kernel + " (untimed: warm-cache or fidelity call)"
+    if kernel.startswith("dense_bf16_kernel") or kernel.startswith("dense_f32_kernel"):
+        if cold:
+            return kernel
+        return kernel + (" (anchor)" if prev.startswith("pddp") else " (untimed)")
     return kernel
 
 
 def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
     """Markdown table of per-kernel durations from a rocprofv3 kernel-trace
-    database (its `kernels` view, read with sqlite3).  Launches of the
-    gathered-attention kernel for the anchor's epilogue and for the
-    block-sparse comparator get rows of their own (launch_label), so that the
-    reuse row is comparable with the live timing of mcs_sparse_attn."""
+    database (its `kernels` view, read with sqlite3).  Launches are split into
+    rows by launch_label, so that the rows of timed calls are comparable with
+    the live timings (reuse_ms_per_call, dense_ms_per_call)."""
     import sqlite3
     con = sqlite3.connect(os.path.abspath(db))
     rows = con.execute("select name, start, end from kernels order by start").fetchall()
@@ -161,10 +174,10 @@ def summarize_trace(db: str, out: str, title: str, cmd: str, note: str) -> None:
 def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: str, cmd_write: str) -> None:
     """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE runs (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB
-    device copy of the same run.  Launches of the gathered-attention kernel
-    for the anchor's epilogue and for the block-sparse comparator are kept
-    apart (launch_label); traffic.json holds the reuse launches.  Writes
-    profiles/traffic.json and a markdown summary."""
+    device copy of the same run.  Launches are split into rows by
+    launch_label; traffic.json holds the rows of timed (cold) calls, the ones
+    the live timings measure.  Writes profiles/traffic.json and a markdown
+    summary."""
     import csv
     per = {}
     for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
