@@ -32,3 +32,21 @@ def test_help_lists_the_contract_flags():
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--config"):
         assert flag in r.stdout
+
+
+def test_launch_labels_follow_the_previous_kernel():
+    """Profile rows: a launch right after the cache-flush fill is a timed call
+    (plain name); the gathered-attention and dense kernels' other launches get
+    rows of their own."""
+    sys.path.insert(0, ROOT)
+    import bench
+    fill = "at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<unsigned char>, std::array<char*, 1ul> >"
+    sp, dn = "sparse_ring_kernel<128, 64>", "dense_bf16_kernel<128, 8>"
+    assert bench.launch_label(sp, fill) == sp
+    assert bench.launch_label(sp, "topk_kernel<512, 64>") == sp + " (anchor epilogue)"
+    assert bench.launch_label(sp, "block_select_sort_kernel<128>") == sp + " (block-sparse comparator)"
+    assert bench.launch_label(sp, sp).endswith("(untimed: warm-cache or fidelity call)")
+    assert bench.launch_label(dn, fill) == dn
+    assert bench.launch_label(dn, "pddp_small_kernel<128>") == dn + " (anchor)"
+    assert bench.launch_label(dn, dn) == dn + " (untimed)"
+    assert bench.launch_label("mass_bf16_kernel<128, 64, 4>", dn) == "mass_bf16_kernel<128, 64, 4>"
