@@ -709,6 +709,9 @@ def main():
                      "frac": round(rbytes / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": rbytes,
+                     # HBM rate of the bytes that really crossed L2 to memory (traffic), against the same peak
+                     "traffic_gbs": round(traffic / (r_mean * 1e-3) / 1e9, 1) if traffic else None,
+                     "traffic_frac": round(traffic / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if traffic else None,
                      "mfma_view_tflops": round(f_reuse / (r_mean * 1e-3) / 1e12, 2)},
         "roofline_dense": {"kernel": "dense_bf16_kernel (mcs_dense_attn)", "bound": "mfma",
                            "achieved": round(f_dense / (d_mean * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
