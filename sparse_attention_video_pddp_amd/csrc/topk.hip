@@ -11,7 +11,8 @@
 // twice the bins of a pass over bits 31..20, half the atomic contention on
 // rows whose masses share few octaves.  Rows of up to 81920 keys are held in
 // registers (up to 64 keys per thread of a 512-thread workgroup, or 80 of a
-// 1024-thread one; one HBM read); longer rows are re-read on each pass.
+// 1024-thread one; one HBM read); longer rows are re-read on each pass,
+// sixteen keys per thread in flight.
 #include "mcs_kernels.hpp"
 #include "select.hpp"
 
