@@ -74,20 +74,17 @@ def test_attention_over_a_foreign_cache(cuda):
         assert_reports(reps, f"cache attention head {h}")
 
 
-def test_largest_kept_key_count(cuda):
-    """The largest supported selection: k = 28672 kept keys per group (the
-    bf16 path's on-chip index table is full) out of a 30240-key cache
-    (472.5 key tiles: a ragged tail), two groups of 64 queries.  The boundary
-    of the top-k then lies deep in the low-mass tail, where near-ties are
-    common; tests/parity.py validates the GPU's choice there."""
+def _foreign_cache_case(kv_grid, k, cfg_id, label):
+    """128 queries (two groups) over a one-head cache of the given grid, k
+    kept keys per group: anchor and reuse on the GPU, every stage checked
+    against the oracle."""
     import torch
     from sparse_attention_video_pddp_amd import mcs
     from sparse_attention_video_pddp_amd.workload import _to_tensor
     from tests.gpu_runner import log
-    wq = WQ.with_(name="maxk_q", H=1, grid=(1, 8, 16))
-    wkv = wq.with_(name="maxk_kv", cfg_id=98, grid=(12, 40, 63))
-    k = 28672
-    assert wkv.Nkv == 30240 and wq.Nq == 128
+    wq = WQ.with_(name="one_head_q", H=1, grid=(1, 8, 16))
+    wkv = wq.with_(name="one_head_kv", cfg_id=cfg_id, grid=kv_grid)
+    assert wq.Nq == 128
     p = mcs.problem(1, 1, wq.Nq, wkv.Nkv, wq.d, wq.group_size, k, wq.scale, dtype=wq.dtype,
                     pddp_iters=wq.pddp_iters)
     q0 = synth.head_inputs(wq, 0, 0, 0)[0]
@@ -108,5 +105,21 @@ def test_largest_kept_key_count(cuda):
                     O_reuse=O1[0, 0].float().cpu().numpy().astype(np.float64))
     reps = check_head(case, wq.group_size, k, wq.scale, 0, 0, wq.pddp_iters)
     for r in reps:
-        log(f"  k = {k} of {wkv.Nkv}: {r}")
-    assert_reports(reps, f"k = {k}")
+        log(f"  {label}: {r}")
+    assert_reports(reps, label)
+
+
+def test_largest_kept_key_count(cuda):
+    """The largest supported selection: k = 28672 kept keys per group (the
+    bf16 path's on-chip index table is full) out of a 30240-key cache
+    (472.5 key tiles: a ragged tail), two groups of 64 queries.  The boundary
+    of the top-k then lies deep in the low-mass tail, where near-ties are
+    common; tests/parity.py validates the GPU's choice there."""
+    _foreign_cache_case((12, 40, 63), 28672, 98, "k = 28672 of 30240 keys")
+
+
+def test_top_k_over_rows_longer_than_the_register_cache(cuda):
+    """Mass rows of 100000 keys: more than the top-k kernel keeps in
+    registers (81920), so its block select re-reads the row from memory on
+    every pass (sixteen keys per thread in flight); every group is checked."""
+    _foreign_cache_case((25, 40, 100), 2000, 99, "k = 2000 of 100000 keys")
