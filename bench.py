@@ -254,11 +254,19 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
             d = vals.setdefault(label, {})
             v = float(r["Counter_Value"])
             d.setdefault(r["Counter_Name"], []).append(v)
+            dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
             if r["Counter_Name"] == "MfmaFlopsBF16":
-                dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
                 d.setdefault("tflops", []).append(v / dt / 1e12 if dt > 0 else 0.0)
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                # GPU-busy cycles of the dispatch (summed over the XCDs) and their rate
+                d.setdefault("mcycles", []).append(v / 1e6)
+                d.setdefault("cyc_per_ns", []).append(v / (dt * 1e9) if dt > 0 else 0.0)
+                d.setdefault("dur_us", []).append(dt * 1e6)
     cols = [("MfmaUtil", "MFMA busy %", 1), ("tflops", "MFMA TFLOP/s", 1), ("LdsUtil", "LDS busy %", 1),
-            ("LdsBankConflict", "bank-conflict cycles per LDS cycle", 3), ("VALUBusy", "VALU busy %", 1)]
+            ("LdsBankConflict", "bank-conflict cycles per LDS cycle", 3), ("VALUBusy", "VALU busy %", 1),
+            ("dur_us", "duration (us)", 1), ("mcycles", "GRBM_GUI_ACTIVE (M cycles)", 2),
+            ("cyc_per_ns", "GRBM_GUI_ACTIVE per ns", 3)]
+    cols = [c for c in cols if any(c[0] in d for d in vals.values())]  # only counters of these runs
     with open(out, "w") as f:
         f.write(f"# {title}\n\nCommands (repository root, one MI355X; one run per counter set):\n\n```\n")
         for _, cmd in runs:
@@ -268,7 +276,8 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
             f.write(note + "\n\n")
         f.write("| kernel | launches | " + " | ".join(c[1] for c in cols) + " |\n|---|---:|" +
                 "---:|" * len(cols) + "\n")
-        for k in sorted(vals, key=lambda k: -statistics.fmean(vals[k].get("MfmaUtil", [0.0]))):
+        order = "MfmaUtil" if any("MfmaUtil" in d for d in vals.values()) else "dur_us"
+        for k in sorted(vals, key=lambda k: -statistics.fmean(vals[k].get(order, [0.0]))):
             d = vals[k]
             n = max(len(v) for v in d.values())
             cells = [f"{statistics.fmean(d[c]):.{nd}f}" if c in d else "" for c, _, nd in cols]
