@@ -673,8 +673,17 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   const int parts = (nd.n + p.cr - 1) / p.cr;
   const size_t node = (size_t)bh * (1 << p.level) + slot;
   const double* src = p.part + node * p.pmax * E + e;
+  // four partials loaded before they are added (four loads in flight), added in chunk order
   double s = 0.0;
-  for (int q = 0; q < parts; ++q) s += src[(size_t)q * E];
+  int q = 0;
+  for (; q + 4 <= parts; q += 4) {
+    double v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = src[(size_t)(q + i) * E];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += v[i];
+  }
+  for (; q < parts; ++q) s += src[(size_t)q * E];
   p.red[node * E + e] = s;
 }
 
