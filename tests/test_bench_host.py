@@ -50,3 +50,61 @@ def test_launch_labels_follow_the_previous_kernel():
     assert bench.launch_label(dn, "pddp_small_kernel<128>") == dn + " (anchor)"
     assert bench.launch_label(dn, dn) == dn + " (untimed)"
     assert bench.launch_label("mass_bf16_kernel<128, 64, 4>", dn) == "mass_bf16_kernel<128, 64, 4>"
+
+
+FILL = "void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<unsigned char>, std::array<char*, 1ul> >(int)"
+SPARSE = "void mcs::(anonymous namespace)::sparse_ring_kernel<128, 64>(mcs::(anonymous namespace)::Params)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _counter_csv(path, rows):
+    """A rocprofv3 counter-collection CSV with the columns the summaries read."""
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        for i, (kernel, counter, value, dur_ns) in enumerate(rows, 1):
+            w.writerow([i, kernel, counter, value, 1000 * i, 1000 * i + dur_ns])
+
+
+def test_traffic_summary_scales_by_the_copy_and_keeps_timed_launches(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE in KiB per dispatch, scaled so that the 1 GiB
+    copy reads 1 GiB; traffic.json takes the timed (post-flush) launches."""
+    sys.path.insert(0, ROOT)
+    import bench
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "hash-" + k)
+    gib_kib = float(1 << 20)
+    fetch = [(COPY, "FETCH_SIZE", gib_kib / 2, 1), (FILL, "FETCH_SIZE", 0.0, 1), (SPARSE, "FETCH_SIZE", 1000.0, 1),
+             (SPARSE, "FETCH_SIZE", 10.0, 1)]            # second sparse launch: not after the fill
+    write = [(COPY, "WRITE_SIZE", gib_kib, 1), (FILL, "WRITE_SIZE", 5.0, 1), (SPARSE, "WRITE_SIZE", 100.0, 1),
+             (SPARSE, "WRITE_SIZE", 1.0, 1)]
+    _counter_csv(tmp_path / "f.csv", fetch)
+    _counter_csv(tmp_path / "w.csv", write)
+    bench.summarize_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cfg", "cmd-f", "cmd-w")
+    import json
+    t = json.load(open(tmp_path / "profiles" / "traffic.json"))["sparse_ring_kernel"]["cfg"]
+    assert t["fetch_factor"] == 2.0 and t["write_factor"] == 1.0 and t["launches"] == 1
+    assert t["fetch_bytes"] == round(1000.0 * 1024 * 2) and t["write_bytes"] == round(100.0 * 1024)
+    assert t["source_hash"] == "hash-sparse_ring_kernel"
+    md = open(tmp_path / "profiles" / "traffic_cfg.md").read()
+    assert "cmd-f" in md and "(untimed: warm-cache or fidelity call)" in md
+
+
+def test_counter_summary_writes_the_cycle_columns(tmp_path):
+    """GRBM_GUI_ACTIVE per dispatch becomes cycles per launch and cycles per
+    ns of the dispatch's own duration; columns of absent counters are left
+    out."""
+    sys.path.insert(0, ROOT)
+    import bench
+    rows = [(FILL, "GRBM_GUI_ACTIVE", 2e3, 100), (SPARSE, "GRBM_GUI_ACTIVE", 8e6, 500000)]
+    _counter_csv(tmp_path / "c.csv", rows)
+    out = tmp_path / "clock.md"
+    bench.summarize_pmc(str(out), [(str(tmp_path / "c.csv"), "the command")], "T", "N")
+    md = open(out).read()
+    assert "GRBM_GUI_ACTIVE (M cycles)" in md and "MFMA busy %" not in md
+    row = [l for l in md.splitlines() if l.startswith("| `sparse_ring_kernel<128, 64>`")][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    assert cells[1] == "1" and cells[2] == "500.0" and cells[3] == "8.00" and cells[4] == "16.000"
