@@ -6,12 +6,18 @@
 // every node is one contiguous range perm[start, start+n) of its head, and
 // the node's shape (start, n, c groups) follows from its slot number alone.
 // For a node with c >= 2 groups:
-//   1. S = sum x and the raw scatter sum x x^T over the node's rows: bf16
-//      rows through v_mfma_f32_32x32x16_bf16 (exact products, fp32 sums over
-//      64-row tiles, fp64 across tiles), fp32 rows with fp64 FMAs;
-//   2. C = sum x x^T - S S^T / n (fp64) and the fixed-step power iteration
+//   1. S = sum y and the scatter sum y y^T over the node's rows, where
+//      y = x - r is the row shifted by the node's first member row r (bf16
+//      inputs; fp32 inputs use r = 0): bf16 rows go through
+//      v_mfma_f32_32x32x16_bf16 as y = hi + lo, two bf16 parts (exact
+//      products, fp32 sums over 64-row tiles, fp64 across tiles), fp32 rows
+//      with fp64 FMAs.  Without the shift, queries sharing a large mean would
+//      make sum x x^T and S S^T / n nearly equal, and their fp32 sums would
+//      lose the spread around the mean that the direction is taken from;
+//   2. C = sum y y^T - S S^T / n (fp64, the same matrix as for x since
+//      centring removes any shift) and the fixed-step power iteration
 //      v <- C v / ||C v|| from v0 = 1/sqrt(d) in fp64 (a zero product keeps v);
-//   3. projections p_i = x_i . v - (S/n) . v in fp64, keyed by float(p_i);
+//   3. projections p_i = x_i . v - (r + S/n) . v in fp64, keyed by float(p_i);
 //   4. the floor(c/2)*G members of smallest key, equal keys lowest position
 //      first, go left, the rest right, both in their previous order (members
 //      stay in ascending token order, so position order is index order).
@@ -62,6 +68,20 @@ struct Node {
   int start, n, c;
 };
 
+// y = x - r as two bf16 parts, hi = bf16(y) and lo = bf16(y - hi).  x and r
+// are bf16 values, so y and y - hi are exact in fp32 and hi + lo equals y
+// whenever y has at most 16 significant bits (otherwise it is within 2^-17
+// of y); products of the parts are exact in the fp32 MFMA accumulators.
+__device__ __forceinline__ void split_shifted(bf16x8 x, float r, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float y = (float)x[j] - r;
+    const __bf16 h = (__bf16)y;
+    hi[j] = h;
+    lo[j] = (__bf16)(y - (float)h);
+  }
+}
+
 // Shape of node `slot` of `level` (c == 0: the slot lies under a leaf).
 __device__ __forceinline__ Node pddp_node(int slot, int level, int Nq, int G) {
   Node nd{0, Nq, (Nq + G - 1) / G};
@@ -97,8 +117,10 @@ struct GramLds {
 };
 
 // Step 1 over member rows [r0, r1) of a node (nperm: the node's members).
-// cacc (waves w < NB): sum x x^T, element (bi, i) = row 32*bi + 8*(i/4) +
-// 4*h + i%4, column 32*w + lane%32.  sS[0..D): sum x.  Ends with a barrier.
+// cacc (waves w < NB): sum y y^T, element (bi, i) = row 32*bi + 8*(i/4) +
+// 4*h + i%4, column 32*w + lane%32.  sS[0..D): sum y.  For bf16 rows
+// y = x - Q[nperm[0]] (the node's first member row), for fp32 rows y = x.
+// Ends with a barrier.
 template <int D, bool BF16>
 __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
                           unsigned char* slot0, unsigned char* slot1, double (&cacc)[D / 32][16], double* sS) {
@@ -121,6 +143,12 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     const int ob1 = (8 + vr) * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(8 + vr));
     const int lrow0 = l / C::CH, lchunk = l % C::CH;
     const int ntiles = (r1 - r0 + 63) / 64;
+    // the shift: this lane's channels of the node's first member row
+    const __bf16* rrow = Qh + (size_t)nperm[0] * D;
+    float rv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rv[b] = (float)rrow[32 * b + ln];
+    const float rw = (float)rrow[32 * min(w, NB - 1) + ln];
     // column sums: lane (n, h) of wave w keeps element n%16 of the ones-product,
     // i.e. S[32w + 8((n%16)/4) + 4h + n%4]
     double sacc = 0.0;
@@ -130,7 +158,8 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
 #pragma unroll
       for (int j = 0; j < C::LPW; ++j) {
         const int r = C::RPL * (w + 4 * j) + lrow0;
-        ids[j] = nperm[min(r0 + t * 64 + r, r1 - 1)];  // tail rows repeat the last row (masked below)
+        const int i = r0 + t * 64 + r;
+        ids[j] = nperm[i < r1 ? i : 0];  // tail rows: the shift row, which shifts to exactly 0
       }
     };
     auto issue = [&](unsigned char* slot) {
@@ -144,43 +173,38 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     bf16x8 ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
-    // x^T operand of channel block b for 16-row step ks2, rows >= valid zeroed
-    auto operand = [&](const unsigned char* slot, int b, int ks2, int valid) {
+    // shifted y^T operand of channel block b (shift r) for 16-row step ks2 as
+    // two bf16 parts (tail rows of the last tile are the shift row: zero)
+    auto operand = [&](const unsigned char* slot, int b, float r, int ks2, bf16x8& hi, bf16x8& lo) {
       const unsigned char* base = slot + 16 * (2 * D) * ks2;
-      bf16x8 op = cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
-      if (valid < 64) {
-        const __bf16 z = (__bf16)0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          op[j] = 16 * ks2 + 4 * h + j < valid ? op[j] : z;
-          op[4 + j] = 16 * ks2 + 8 + 4 * h + j < valid ? op[4 + j] : z;
-        }
-      }
-      return op;
+      split_shifted(cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b)))), r, hi, lo);
     };
-    // two fp32 accumulators live at a time (row blocks outer), which keeps the
-    // kernel within 256 registers per lane
-    auto compute = [&](const unsigned char* slot, int valid) {
+    // one fp32 accumulator live at a time (row blocks outer) and this wave's
+    // own operand re-read for each block, which keeps the kernel within 256
+    // registers per lane (a chain of dependent MFMAs issues as fast as
+    // independent ones); y y^T = (hi + lo)(hi + lo)^T as four exact products
+    auto compute = [&](const unsigned char* slot) {
       if (w >= NB) return;
-      bf16x8 ow[4];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) ow[ks2] = operand(slot, w, ks2, valid);
       f32x16 accS = {};
 #pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) accS = mfma_32x32x16(ow[ks2], ones, accS);
-#pragma unroll
-      for (int bi = 0; bi < NB; bi += 2) {  // two independent accumulators
-        f32x16 acc0 = {}, acc1 = {};
+      for (int bi = 0; bi < NB; ++bi) {
+        f32x16 acc = {};
 #pragma unroll
         for (int ks2 = 0; ks2 < 4; ++ks2) {
-          acc0 = mfma_32x32x16(operand(slot, bi, ks2, valid), ow[ks2], acc0);
-          acc1 = mfma_32x32x16(operand(slot, bi + 1, ks2, valid), ow[ks2], acc1);
+          bf16x8 wh, wl, hb, lb;
+          operand(slot, w, rw, ks2, wh, wl);
+          operand(slot, bi, rv[bi], ks2, hb, lb);
+          acc = mfma_32x32x16(hb, wh, acc);
+          acc = mfma_32x32x16(hb, wl, acc);
+          acc = mfma_32x32x16(lb, wh, acc);
+          acc = mfma_32x32x16(lb, wl, acc);
+          if (bi == 0) {
+            accS = mfma_32x32x16(wh, ones, accS);
+            accS = mfma_32x32x16(wl, ones, accS);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          cacc[bi][i] += (double)acc0[i];
-          cacc[bi + 1][i] += (double)acc1[i];
-        }
+        for (int i = 0; i < 16; ++i) cacc[bi][i] += (double)acc[i];
       }
       float sv = accS[0];
 #pragma unroll
@@ -199,7 +223,7 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
         issue(slot1);
         if (t + 2 < ntiles) load_ids(t + 2);
       }
-      compute(slot0, r1 - r0 - t * 64);
+      compute(slot0);
       if (t + 1 >= ntiles) break;
       wait_vmcnt<0>();
       __syncthreads();
@@ -207,7 +231,7 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
         issue(slot0);
         if (t + 3 < ntiles) load_ids(t + 3);
       }
-      compute(slot1, r1 - r0 - (t + 1) * 64);
+      compute(slot1);
     }
     if (w < NB && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = sacc;
     __syncthreads();
@@ -243,14 +267,16 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
   }
 }
 
-// Step 2.  cacc holds sum x x^T (layout of gram_rows), sS the column sums
-// (visible to all threads).  Leaves v in sV and returns (S/n) . v.
+// Step 2.  cacc holds sum y y^T (layout of gram_rows), sS the column sums
+// of y = x - r and sR the shift r (NULL: r = 0), both visible to all
+// threads.  Leaves v in sV and returns the node mean's projection
+// (r + S/n) . v.
 // With v_k = y_k / ||y_k||, the iteration runs as y_{k+1} = C y_k / ||y_k||:
 // the norm of y_k is reduced while y_{k+1} is formed, so one barrier per step
 // suffices (y double-buffered in sY).  If C v_k = 0 the direction stays v_k.
 template <int D>
-__device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* sS, double* sV, double (*sY)[D],
-                                     double (*sRed)[4], int n, int iters) {
+__device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* sS, const double* sR, double* sV,
+                                     double (*sY)[D], double (*sRed)[4], int n, int iters) {
   constexpr int NB = D / 32;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
   const bool gw = w < NB;
@@ -302,7 +328,7 @@ __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* s
   const double inv = 1.0 / sqrt(nl);
   if (tid < D) sV[tid] = sY[last][tid] * inv;
   __syncthreads();
-  const double mv = wave_sum_f64(tid < D ? sS[tid] * inv_n * sV[tid] : 0.0);
+  const double mv = wave_sum_f64(tid < D ? ((sR ? sR[tid] : 0.0) + sS[tid] * inv_n) * sV[tid] : 0.0);
   if (l == 0 && w < 4) sRed[cur ^ 1][w] = mv;  // buffer no longer read
   __syncthreads();
   const double muv = (sRed[cur ^ 1][0] + sRed[cur ^ 1][1]) + (sRed[cur ^ 1][2] + sRed[cur ^ 1][3]);
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   using Sel = BlockSelect<kNodeThreads, VPT>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[L::SLOT0];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
-  __shared__ double sS[D], sV[D], sY[2][D], sRed[2][4];
+  __shared__ double sS[D], sR[D], sV[D], sY[2][D], sRed[2][4];
   __shared__ typename Sel::Shared sh;
   __shared__ uint32_t s_keys[VPT * kNodeThreads];
   const int bh = blockIdx.y;
@@ -414,9 +440,10 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   if (nd.c <= 1) return;
   const size_t hbase = (size_t)bh * p.Nq;
   int32_t* nperm = p.perm + hbase + nd.start;
+  if (BF16 && (int)threadIdx.x < D) sR[threadIdx.x] = (double)(float)((const __bf16*)p.Q)[(hbase + nperm[0]) * D + threadIdx.x];
   double cacc[D / 32][16];
-  gram_rows<D, BF16>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, cacc, sS);
-  const double muv = centre_and_iterate<D>(cacc, sS, sV, sY, sRed, nd.n, p.iters);
+  gram_rows<D, BF16>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, cacc, sS);  // its final barrier publishes sR
+  const double muv = centre_and_iterate<D>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
   project_rows<D, BF16, kNodeThreads>(p.Q, hbase, nperm, 0, nd.n, sV, muv, [&](int i, uint32_t k) { s_keys[i] = k; });
   __syncthreads();
   Sel sel;
@@ -438,10 +465,12 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 // ---- small nodes ------------------------------------------------------------
 // Nodes of at most kSmallRows rows (the deep levels: thousands of nodes, each a
 // chain of latencies) run with a lighter state so that four workgroups share a
-// CU: the scatter sums of all tiles stay in the fp32 MFMA accumulators (exact
-// bf16 products, fp32 sums over at most kSmallRows rows), the centring is
-// done in fp64 and the power iteration runs in fp32 (C rounded to fp32); the
-// projections stay fp64.  K tiles of 32 rows in a two-slot ring of 8 KB.
+// CU: the scatter sums of the shifted rows y = x - r (r: the node's first
+// member row; y = hi + lo in two bf16 parts, see split_shifted) stay in the
+// fp32 MFMA accumulators over all tiles (exact products, fp32 sums over at
+// most kSmallRows rows), the centring is done in fp64 and the power iteration
+// runs in fp32 (C rounded to fp32); the projections stay fp64.  Row tiles of
+// 32 rows in a two-slot ring of 8 KB.
 constexpr int kSmallRows = 512;
 
 template <int D>
@@ -457,7 +486,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   using Sel = BlockSelect<kNodeThreads, VPT>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[TILE];
-  __shared__ double sS[D], sV[D], sMu[4];
+  __shared__ double sS[D], sR[D], sV[D], sMu[4];
   __shared__ float sY[2][D], sRed[2][4];
   __shared__ typename Sel::Shared sh;
   __shared__ uint32_t s_keys[kSmallRows];
@@ -471,8 +500,14 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const bool gw = w < NB;
 
-  // ---- 1. scatter sums, fp32 over all tiles ---------------------------------
+  // ---- 1. scatter sums of the shifted rows, fp32 over all tiles ---------------
   const __bf16* Qh = (const __bf16*)p.Q + hbase * D;
+  const __bf16* rrow = Qh + (size_t)nperm[0] * D;  // the shift r
+  if (tid < D) sR[tid] = (double)(float)rrow[tid];
+  float rv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rv[b] = (float)rrow[32 * b + ln];
+  const float rw = (float)rrow[32 * min(w, NB - 1) + ln];
   const int vr = 4 * h + ((l & 15) >> 2);
   const int c0 = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
   const int ob0 = vr * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(vr));
@@ -482,7 +517,10 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   int ids[LPW];
   auto load_ids = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) ids[j] = nperm[min(t * TR + RPL * (wu + 4 * j) + lrow0, n - 1)];
+    for (int j = 0; j < LPW; ++j) {
+      const int i = t * TR + RPL * (wu + 4 * j) + lrow0;
+      ids[j] = nperm[i < n ? i : 0];  // tail rows: the shift row, which shifts to exactly 0
+    }
   };
   auto issue = [&](unsigned char* slot) {
 #pragma unroll
@@ -497,37 +535,27 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   f32x16 acc[NB], accS = {};
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-  auto compute = [&](const unsigned char* slot, int valid) {
+  auto compute = [&](const unsigned char* slot) {
     if (!gw) return;
 #pragma unroll
     for (int ks2 = 0; ks2 < TR / 16; ++ks2) {
       const unsigned char* base = slot + 16 * (2 * D) * ks2;
-      bf16x8 op[NB];
+      auto part = [&](int b, float r, bf16x8& hi, bf16x8& lo) {
+        split_shifted(cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b)))), r, hi, lo);
+      };
+      bf16x8 wh, wl;  // this wave's column block
+      part(w, rw, wh, wl);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) op[b] = cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
-      if (valid < TR) {
-        const __bf16 z = (__bf16)0.0f;
-        // rows of this lane relative to the tail, recomputed here (an opaque
-        // copy keeps the compiler from hoisting the comparisons out of the
-        // tile loop and spilling them)
-        int rel = valid - 16 * ks2 - 4 * h;
-        asm volatile("" : "+v"(rel));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool k0 = j < rel, k1 = 8 + j < rel;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            op[b][j] = k0 ? op[b][j] : z;
-            op[b][4 + j] = k1 ? op[b][4 + j] : z;
-          }
-        }
+      for (int bi = 0; bi < NB; ++bi) {
+        bf16x8 hb, lb;
+        part(bi, rv[bi], hb, lb);
+        acc[bi] = mfma_32x32x16(hb, wh, acc[bi]);
+        acc[bi] = mfma_32x32x16(hb, wl, acc[bi]);
+        acc[bi] = mfma_32x32x16(lb, wh, acc[bi]);
+        acc[bi] = mfma_32x32x16(lb, wl, acc[bi]);
       }
-      bf16x8 ow = op[0];
-#pragma unroll
-      for (int b = 1; b < NB; ++b) ow = (b == w) ? op[b] : ow;
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi) acc[bi] = mfma_32x32x16(op[bi], ow, acc[bi]);
-      accS = mfma_32x32x16(ow, ones, accS);
+      accS = mfma_32x32x16(wh, ones, accS);
+      accS = mfma_32x32x16(wl, ones, accS);
     }
   };
   load_ids(0);
@@ -540,7 +568,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       issue(slot1);
       if (t + 2 < ntiles) load_ids(t + 2);
     }
-    compute(slot0, n - t * TR);
+    compute(slot0);
     if (t + 1 >= ntiles) break;
     wait_vmcnt<0>();
     __syncthreads();
@@ -548,7 +576,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       issue(slot0);
       if (t + 3 < ntiles) load_ids(t + 3);
     }
-    compute(slot1, n - (t + 1) * TR);
+    compute(slot1);
   }
   // column sums: lane (n, h) of wave w keeps element n%16: S[32w + 8((n%16)/4) + 4h + n%4]
   {
@@ -608,7 +636,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   const double vinv = 1.0 / sqrt((double)nl);
   if (tid < D) sV[tid] = (double)sY[last][tid] * vinv;
   __syncthreads();
-  const double mv = wave_sum_f64(tid < D ? sS[tid] * inv_n * sV[tid] : 0.0);
+  const double mv = wave_sum_f64(tid < D ? (sR[tid] + sS[tid] * inv_n) * sV[tid] : 0.0);
   if (l == 0 && w < 4) sMu[w] = mv;
   __syncthreads();
   const double muv = (sMu[0] + sMu[1]) + (sMu[2] + sMu[3]);
@@ -687,10 +715,10 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   p.red[node * E + e] = s;
 }
 
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) {
   constexpr int E = D + D * D;
-  __shared__ double sS[D], sV[D], sY[2][D], sRed[2][4];
+  __shared__ double sS[D], sR[D], sV[D], sY[2][D], sRed[2][4];
   const int bh = blockIdx.y, slot = blockIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
   if (nd.c <= 1) return;
@@ -699,6 +727,9 @@ __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
   double cacc[D / 32][16];
   if (tid < D) sS[tid] = red[tid];
+  // the shift of the partial sums: the node's first member row (bf16 inputs)
+  const size_t hbase = (size_t)bh * p.Nq;
+  if (BF16 && tid < D) sR[tid] = (double)(float)((const __bf16*)p.Q)[(hbase + p.perm[hbase + nd.start]) * D + tid];
   if (w < D / 32) {
 #pragma unroll
     for (int bi = 0; bi < D / 32; ++bi)
@@ -707,7 +738,7 @@ __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) 
         cacc[bi][i] = red[D + (size_t)(32 * bi + 8 * (i >> 2) + 4 * h + (i & 3)) * D + 32 * w + ln];
   }
   __syncthreads();
-  const double muv = centre_and_iterate<D>(cacc, sS, sV, sY, sRed, nd.n, p.iters);
+  const double muv = centre_and_iterate<D>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
   double* out = p.vec + node * (D + 1);
   if (tid < D) out[tid] = sV[tid];
   if (tid == 0) out[D] = muv;
@@ -837,7 +868,7 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
       const dim3 chunks(nslots * p.pmax, s.BH);
       hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
       hipLaunchKernelGGL((pddp_reduce_kernel<D>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
-      hipLaunchKernelGGL((pddp_power_kernel<D>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
+      hipLaunchKernelGGL((pddp_power_kernel<D, BF16>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
       p.pj_pmax = (int)((maxn + kProjRows - 1) / kProjRows);
       hipLaunchKernelGGL((pddp_project_kernel<D, BF16>), dim3(nslots * p.pj_pmax, s.BH), dim3(256), 0, st, p);
       if (maxn <= 64LL * kSplitThreads)

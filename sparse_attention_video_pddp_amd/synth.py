@@ -17,6 +17,11 @@ makes token-level selection meaningful.
   Q and K add independent 0.2 N(0, 1) noise.
 * Drift between denoising steps: a cumulative random walk
   X_{t+1} = X_t + sigma N(0, 1) for each of Q, K, V.
+* Optional query offset (test workloads only): Q += q_mean * m with
+  m_c = 1 + 0.5 z_c, z ~ N(0, 1) per head and channel, i.e. a mean shared by
+  every query along the all-ones direction plus a per-channel spread, tens of
+  times the queries' own spread.  Grouping must centre each node on its mean;
+  this makes any loss of precision in that step visible.
 
 Tokens are flattened frame-major, n = (t * height + y) * width + x, following
 the per-axis (f, h, w) block alignment in the MonarchRT summary (section 2).
@@ -41,6 +46,7 @@ import numpy as np
 ROLE_W, ROLE_PHASE, ROLE_EPS_Q, ROLE_EPS_K, ROLE_V = 0, 1, 2, 3, 4
 ROLE_DRIFT_Q, ROLE_DRIFT_K, ROLE_DRIFT_V = 5, 6, 7
 ROLE_FIELD, ROLE_NOISE_Q, ROLE_NOISE_K = 8, 9, 10
+ROLE_Q_MEAN = 11
 
 
 @dataclasses.dataclass(frozen=True)
@@ -64,6 +70,7 @@ class Workload:
     field_sigma: float = 2.0
     field_noise: float = 0.2
     drift: float = 0.03
+    q_mean: float = 0.0         # common query offset (see head_base); 0 for the benchmark workloads
     steps: int = 2
     anchor_every: int = 1 << 30
     pddp_iters: int = 32
@@ -215,6 +222,9 @@ def head_base(w: Workload, b: int, h: int) -> Tuple[np.ndarray, np.ndarray, np.n
         K = field + w.field_noise * _rng(w, ROLE_NOISE_K, bh, 0).standard_normal(field.shape)
     else:
         raise ValueError(f"unknown generator {w.generator!r}")
+    if w.q_mean:
+        m = 1.0 + 0.5 * _rng(w, ROLE_Q_MEAN, bh, 0).standard_normal(w.d)
+        Q = Q + w.q_mean * m[None, :]
     V = _rng(w, ROLE_V, bh, 0).standard_normal((w.Nkv, w.d))
     return Q, K, V
 

@@ -37,6 +37,17 @@ SMALL = {
     # bf16, d=64 with groups of 64 (the stress workload has G=128): 960 tokens -> 15 groups, k=144
     "d64_g64": synth.get("bidir5").with_(name="d64_g64", H=2, d=64, grid=(4, 12, 20), keep_permille=150,
                                          scale=1.0 / 8.0),
+    # queries sharing a mean far from the origin (30 x (1 + 0.5 z) per channel, ~40x the queries' own
+    # spread): PDDP must centre each node without losing the spread.  4960 tokens, so the top
+    # levels run the many-workgroup scatter kernels, the middle ones the one-workgroup node
+    # kernel and the deep ones the small-node kernel; a mild logit scale keeps the attention
+    # stages away from underflowing masses.  bf16, d=128, G=64 (78 groups, last 32), k=248
+    "offset_d128_g64": synth.get("bidir5").with_(name="offset_d128_g64", H=2, grid=(8, 20, 31), keep_permille=50,
+                                                 q_mean=30.0, scale=0.1 / 128 ** 0.5),
+    # the same offset with d=64 and G=128: 2640 tokens (21 groups, last 80), k=264
+    "offset_d64_g128": synth.get("bidir5").with_(name="offset_d64_g128", H=2, d=64, group_size=128,
+                                                 grid=(6, 20, 22), keep_permille=100, q_mean=30.0,
+                                                 scale=0.1 / 8.0),
     # fp32, d=128 with groups of 128, frame-causal: 900 queries of 1200 keys, k=120
     "f32_d128_g128": synth.get("tiny").with_(name="f32_d128_g128", H=2, d=128, group_size=128,
                                              grid=(8, 10, 15), q_frames=(2, 8), causal_block=150,

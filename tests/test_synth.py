@@ -79,3 +79,17 @@ def test_field_generator_statistics():
     # smooth field: adjacent x tokens correlate ~exp(-1/(4 sigma^2)) ~ 0.94
     c = np.mean(np.sum(q[:-1] * q[1:], axis=1)) / 64
     assert c > 0.7
+
+
+def test_query_mean_offset():
+    """q_mean shifts every query of a head by the same vector 30 (1 + 0.5 z),
+    leaving K, V and the spread of Q unchanged."""
+    w0 = synth.get("bidir5").with_(name="x", H=1, grid=(2, 6, 8))
+    w1 = w0.with_(q_mean=30.0)
+    q0, k0, v0 = synth.head_base(w0, 0, 0)
+    q1, k1, v1 = synth.head_base(w1, 0, 0)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    shift = q1 - q0
+    assert np.allclose(shift, shift[0][None, :], atol=1e-9)
+    assert 20.0 < shift[0].mean() < 40.0 and shift[0].std() > 5.0
+    assert np.allclose(q1.std(axis=0), q0.std(axis=0), atol=1e-9)
