@@ -101,6 +101,25 @@ def load_traffic(kernel: str, config: str):
     return e.get("bytes_per_launch")
 
 
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock.json")
+N_XCD = 8  # GRBM_GUI_ACTIVE is summed over the chip's XCDs
+
+
+def load_clock(kernel: str, config: str):
+    """Engine clock (MHz) during the kernel's timed launches, from
+    GRBM_GUI_ACTIVE per ns of a counter run on the current kernel source;
+    else None."""
+    try:
+        with open(CLOCK_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel, {}).get(config)
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return e.get("mhz")
+
+
 def _short_kernel(name: str) -> str:
     import re
     m = re.match(r"_ZN3mcs12_GLOBAL__N_1(\d+)", name)
@@ -267,6 +286,24 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
             ("dur_us", "duration (us)", 1), ("mcycles", "GRBM_GUI_ACTIVE (M cycles)", 2),
             ("cyc_per_ns", "GRBM_GUI_ACTIVE per ns", 3)]
     cols = [c for c in cols if any(c[0] in d for d in vals.values())]  # only counters of these runs
+    config = os.environ.get("MCS_BENCH_CONFIG", "bidir5")
+    clock = {}
+    for k, d in vals.items():
+        base = k.split("<")[0]
+        if "cyc_per_ns" in d and base in KERNEL_SOURCES and "(" not in k:  # timed launches only
+            clock.setdefault(base, {})[config] = {
+                "mhz": round(statistics.fmean(d["cyc_per_ns"]) / N_XCD * 1e3, 1),
+                "launches": len(d["cyc_per_ns"]), "source_hash": kernel_source_hash(base)}
+    if clock:
+        try:
+            with open(CLOCK_FILE) as fh:
+                table = json.load(fh)
+        except (OSError, ValueError):
+            table = {}
+        for base, e in clock.items():
+            table.setdefault(base, {}).update(e)
+        with open(CLOCK_FILE, "w") as fh:
+            json.dump(table, fh, indent=1, sort_keys=True)
     with open(out, "w") as f:
         f.write(f"# {title}\n\nCommands (repository root, one MI355X; one run per counter set):\n\n```\n")
         for _, cmd in runs:
@@ -306,12 +343,12 @@ def device_max_sclk_mhz() -> float:
 
 
 def reuse_bytes_per_launch(w) -> float:
-    """Algorithmic bytes of one mcs_sparse_attn call: per (b,h,group) the k
-    gathered K and V rows, the group's Q, R and O rows (all in the input
-    dtype) and the k indices (int32)."""
+    """Logical bytes of one mcs_sparse_attn call: per (b,h,group) the k
+    gathered K and V rows and the group's Q and O rows (input dtype), its R
+    rows (float32) and the k indices (int32)."""
     e = 2 if w.dtype == "bf16" else 4
     BH = w.B * w.H
-    return BH * (w.n_groups * (2 * w.k * w.d * e + 4 * w.k) + w.Nq * w.d * 3 * e)
+    return BH * (w.n_groups * (2 * w.k * w.d * e + 4 * w.k) + w.Nq * w.d * (2 * e + 4))
 
 
 def dense_flops(w) -> float:
@@ -333,15 +370,17 @@ def cpu_baseline(w, host0, host1, nheads: int, reuse_budget_s: float = 10.0):
     """The oracle as it stands, on a bounded sample: its own anchor (PDDP,
     dense attention, column mass, top-k, residual) prepares each sampled
     head, then its reuse step (the metric's operation) is timed, repeated
-    until about reuse_budget_s seconds per head are timed."""
+    until about reuse_budget_s seconds per head are timed, and its dense
+    attention (the comparator) once on the same step-1 inputs.  The value is
+    in the metric's unit: executed FLOPs of the reuse step per second."""
     import numpy as np
-    from oracle.mcs_oracle import anchor_step, reuse_step
+    from oracle.mcs_oracle import anchor_step, dense_attention, reuse_step
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
     heads = sorted(host0)[:nheads]
-    t_anchor = t_reuse = 0.0
+    t_anchor = t_reuse = t_dense = 0.0
     runs = 0  # head reuse steps timed
     for bh in heads:
         q0, k0, v0 = (x.astype(np.float64) for x in host0[bh])
@@ -358,16 +397,24 @@ def cpu_baseline(w, host0, host1, nheads: int, reuse_budget_s: float = 10.0):
             if t_head >= reuse_budget_s:
                 break
         t_reuse += t_head
-    per_head = dense_flops(w) / (w.B * w.H)
+        t1 = time.perf_counter()
+        dense_attention(q1, k1, v1, w.scale, w.causal_block, w.q_offset)
+        t_dense += time.perf_counter() - t1
+    BH = w.B * w.H
     n = len(heads)
     per_run = t_reuse / runs
-    return {"value": round(per_head / per_run / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.B * w.H} heads of {w.name}: the oracle's reuse step (numpy fp64 gathered sparse "
-                      f"attention + R, on the oracle's own anchor of step 0) on step-1 inputs, run {runs} times; "
-                      f"{t_reuse:.1f} s timed ({per_run * 1e3:.0f} ms per head step) after {t_anchor:.1f} s of "
-                      f"oracle anchor work; dense-equivalent FLOPs",
-            "reuse_ms_per_call_extrapolated": round(per_run * w.B * w.H * 1e3, 1),
-            "anchor_ms_per_call_extrapolated": round(t_anchor / n * w.B * w.H * 1e3, 1),
+    return {"value": round(reuse_flops(w) / BH / per_run / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} of {BH} heads of {w.name}: the oracle's reuse step (numpy fp64 gathered sparse "
+                      f"attention + R, on the oracle's own anchor of step 0) on step-1 inputs, run {runs} times, "
+                      f"{t_reuse:.1f} s timed ({per_run * 1e3:.0f} ms per head step); its dense attention once per "
+                      f"head on the same inputs ({t_dense / n * 1e3:.0f} ms per head), after {t_anchor:.1f} s of "
+                      f"oracle anchor work; value = executed reuse FLOPs (4 Nq k d per head) per second",
+            "reuse_ms_per_head": round(per_run * 1e3, 1),
+            "dense_ms_per_head": round(t_dense / n * 1e3, 1),
+            "reuse_ms_per_call_extrapolated": round(per_run * BH * 1e3, 1),
+            "dense_ms_per_call_extrapolated": round(t_dense / n * BH * 1e3, 1),
+            "anchor_ms_per_call_extrapolated": round(t_anchor / n * BH * 1e3, 1),
             "cpu": platform.processor() or platform.machine(), "numpy": np.__version__}
 
 
@@ -549,6 +596,27 @@ def main():
     torch.cuda.synchronize()
     dense_ms = [a.elapsed_time(b) for a, b in dense_ms]
 
+    # the reuse step with the residual stored in bf16 (r_dtype MCS_BF16, opt-in):
+    # its own anchor (untimed), then the same cold protocol and count
+    p16 = mcs.problem_for(w, "bf16") if w.dtype == "bf16" else None
+    r16_ms = []
+    if p16 is not None:
+        st16 = mcs.MCSparseAttention(p16)
+        st16.step(*step_in[0], True, stream=stream)
+        torch.cuda.synchronize()
+        r16_ev = []
+        for i in range(max(1, len(reuse_ms) // 2)):
+            s = 1 + i % (A - 1)
+            a, b = ev(), ev()
+            flush()
+            a.record(stream)
+            mcs.sparse_attn(p16, *step_in[s], st16.perm, st16.idx, st16.R, st16.O, stream=stream)
+            b.record(stream)
+            r16_ev.append((a, b))
+        torch.cuda.synchronize()
+        r16_ms = [a.elapsed_time(b) for a, b in r16_ev]
+        del st16
+
     # block-sparse comparator at the same token budget: mean-pooled block
     # selection from the step's own Q/K, then the gathered attention (no residual)
     bsa = mcs.BlockSparseComparator(p)
@@ -572,7 +640,7 @@ def main():
     # residual-drift check of adaptive anchoring (64 sampled rows per head) on
     # a reuse output, same cold protocol
     drift_rows = torch.tensor(mcs.drift_rows(w.Nq, 64), dtype=torch.int32, device=dev)
-    drift = torch.zeros((w.B, w.H), dtype=torch.float32, device=dev)
+    drift = torch.zeros(w.B * w.H + 1, dtype=torch.float32, device=dev)  # per head, then their maximum
     ws_drift = torch.empty(max(mcs.workspace_size(p, mcs.MCS_WS_DRIFT)[0], 1), dtype=torch.uint8, device=dev)
     mcs.residual_drift(p, *step_in[1], st.O, drift_rows, drift, ws_drift, stream=stream)
     torch.cuda.synchronize()
@@ -610,7 +678,7 @@ def main():
             mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, st.R, st.O, stream=stream)
             fid_r.append(rel(st.O))
             mcs.residual_drift(p, *step_in[s], st.O, drift_rows, drift, ws_drift, stream=stream)
-            fid_drift.append(round(float(drift.max().item()), 6))
+            fid_drift.append(round(float(drift[-1].item()), 6))
             mcs.sparse_attn(p, *step_in[s], st.perm, st.idx, None, On, stream=stream)
             fid_nor.append(rel(On))
             fid_stale.append(rel(O0))
@@ -660,13 +728,17 @@ def main():
 
     f_dense, f_reuse = dense_flops(w), reuse_flops(w)
     r_mean = statistics.fmean(reuse_ms)
-    d_mean = statistics.fmean(dense_ms)
-    value = f_dense / (r_mean * 1e-3) / 1e12
+    d_mean, d_med, d_min = statistics.fmean(dense_ms), statistics.median(dense_ms), min(dense_ms)
+    exec_tflops = f_reuse / (r_mean * 1e-3) / 1e12       # the reuse step's executed rate: the value
+    dense_eq = f_dense / (r_mean * 1e-3) / 1e12          # the dense work it stands in for, per second
+    dense_tflops = f_dense / (d_mean * 1e-3) / 1e12
     rbytes = reuse_bytes_per_launch(w)
     traffic = load_traffic("sparse_ring_kernel", w.name)
+    mhz = load_clock("dense_bf16_kernel", w.name)
+    peak_clk = cus * mhz * 1e6 * 4096 / 1e12 if cus and mhz else None
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(exec_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -680,20 +752,28 @@ def main():
         "config": {"workload": f"{w.name}: full bidirectional 3D attention over a {w.grid[0]}x{w.grid[1]}x"
                                f"{w.grid[2]} = {w.Nkv}-token video latent, B={w.B}, H={w.H}, d={w.d}, "
                                f"{w.dtype}, PDDP groups of {w.group_size}, keep {w.keep_permille / 10:g}% "
-                               f"(k={w.k}), anchor every {A} steps, drift {w.drift} N(0,1) per step",
+                               f"(k={w.k}), anchor every {A} steps, drift {w.drift} N(0,1) per step, "
+                               f"residual R in float32",
                    "B": w.B, "H": w.H, "N": w.Nkv, "d": w.d, "group_size": w.group_size, "k": w.k,
-                   "anchor_every": A},
+                   "anchor_every": A, "residual": "float32"},
         "step": f"one anchor period: mcs_group + mcs_anchor on step 0, mcs_sparse_attn on steps 1..{A - 1}",
+        "value_is": "executed TFLOP/s of the reuse step (mcs_sparse_attn): 4*Nq*k*d*H FLOPs per call over the "
+                    "mean cold call time",
         "reuse_ms_per_call": round(r_mean, 4),
         "reuse_ms_median": round(statistics.median(reuse_ms), 4),
         "reuse_ms_min": round(min(reuse_ms), 4),
-        "reuse_effective_tflops_dense_equiv": round(value, 2),
-        "reuse_effective_frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "reuse_executed_tflops": round(f_reuse / (r_mean * 1e-3) / 1e12, 2),
-        "reuse_executed_frac_bf16_peak": round(f_reuse / (r_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "reuse_executed_tflops": round(exec_tflops, 2),
+        "reuse_executed_frac_bf16_peak": round(exec_tflops / PEAK_BF16_TFLOPS, 4),
+        "reuse_dense_equivalent_tflops": round(dense_eq, 2),
+        "reuse_bf16_residual_ms_per_call": round(statistics.fmean(r16_ms), 4) if r16_ms else None,
+        "reuse_bf16_residual_ms_median": round(statistics.median(r16_ms), 4) if r16_ms else None,
         "dense_ms_per_call": round(d_mean, 4),
-        "dense_tflops": round(f_dense / (d_mean * 1e-3) / 1e12, 2),
-        "dense_frac_bf16_peak": round(f_dense / (d_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dense_ms_median": round(d_med, 4),
+        "dense_ms_min": round(d_min, 4),
+        "dense_tflops": round(dense_tflops, 2),
+        "dense_frac_bf16_peak": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
+        "dense_frac_bf16_peak_median": round(f_dense / (d_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dense_frac_bf16_peak_min_time": round(f_dense / (d_min * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "speedup_reuse_vs_dense": round(d_mean / r_mean, 2),
         "cache": "flushed (512 MB overwrite before every timed call)" if not args.no_flush else "not flushed",
         "fidelity_rel_err_with_R": fid_r or None,
@@ -710,26 +790,38 @@ def main():
         "device_cus": cus,
         "device_max_sclk_mhz": sclk_mhz,
         "peak_bf16_tflops_from_device": round(cus * sclk_mhz * 1e6 * 4096 / 1e12, 1) if cus and sclk_mhz else None,
+        # the engine clock measured during timed dense launches (GRBM_GUI_ACTIVE per ns of a counter run
+        # on the current kernel, profiles/clock.json) and the bf16 peak at that clock
+        "sclk_mhz_measured_dense": mhz,
+        "peak_bf16_tflops_at_measured_clock": round(peak_clk, 1) if peak_clk else None,
+        "dense_frac_at_measured_clock": round(dense_tflops / peak_clk, 4) if peak_clk else None,
         "group_ms": round(statistics.fmean(group_ms), 4),
         "anchor_ms": round(statistics.fmean(anchor_ms), 4),
         "period_effective_tflops_dense_equiv": round(A * f_dense / (wall / args.steps) / 1e12, 2),
-        "roofline": {"kernel": "sparse_ring_kernel (mcs_sparse_attn, reuse step)", "bound": "hbm",
-                     "achieved": round(rbytes / (r_mean * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(rbytes / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        # the reuse kernel against the bf16 MFMA peak on the FLOPs it executes; its HBM rate is from
+        # counter-measured bytes (traffic), and the rate of its logical gathers (most served by L2 and
+        # the Infinity Cache, so above any HBM figure) is reported apart, never as a fraction
+        "roofline": {"kernel": "sparse_ring_kernel (mcs_sparse_attn, reuse step)", "bound": "mfma",
+                     "achieved": round(exec_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(exec_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": rbytes,
-                     # HBM rate of the bytes that really crossed L2 to memory (traffic), against the same peak
+                     "executed_flops_per_launch": f_reuse,
+                     "frac_at_measured_clock": round(exec_tflops / peak_clk, 4) if peak_clk else None,
                      "traffic_gbs": round(traffic / (r_mean * 1e-3) / 1e9, 1) if traffic else None,
                      "traffic_frac": round(traffic / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if traffic else None,
-                     "mfma_view_tflops": round(f_reuse / (r_mean * 1e-3) / 1e12, 2)},
+                     "logical_gather_bytes_per_launch": rbytes,
+                     "logical_gather_gbs": round(rbytes / (r_mean * 1e-3) / 1e9, 1)},
         "roofline_dense": {"kernel": "dense_bf16_kernel (mcs_dense_attn)", "bound": "mfma",
-                           "achieved": round(f_dense / (d_mean * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(f_dense / (d_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "achieved": round(dense_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
                            "traffic": load_traffic("dense_bf16_kernel", w.name)},
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, host[0], host[1], args.cpu_heads)
+        cb = cpu_baseline(w, host[0], host[1], args.cpu_heads)
+        cb["gpu_over_oracle_reuse"] = round(cb["reuse_ms_per_call_extrapolated"] / r_mean, 1)
+        cb["gpu_over_oracle_dense"] = round(cb["dense_ms_per_call_extrapolated"] / d_mean, 1)
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

@@ -22,8 +22,8 @@
  *  - Layouts are row-major: Q [B,H,Nq,d], K and V [B,H,Nkv,d], O [B,H,Nq,d]
  *    (d fastest).  Tokens of a (frames x height x width) latent are flattened
  *    frame-major, n = (t*height + y)*width + x.
- *  - Q, K, V, O and the residual R have element type `dtype`; lse and scores
- *    are float32.
+ *  - Q, K, V and O have element type `dtype`; the residual R is float32
+ *    unless `r_dtype` asks for bf16; lse and scores are float32.
  *  - Query row i sits at position q_offset + i of the KV sequence.  With
  *    causal_block == 0 every key is visible; otherwise key j is visible to
  *    query i iff j / causal_block <= (q_offset + i) / causal_block
@@ -62,10 +62,11 @@ typedef enum mcs_workspace_kind {
 } mcs_workspace_kind;
 
 /* Problem description.  Supported: d in {64,128}; group_size in {64,128};
- * 1 <= k <= Nkv, and k <= 28672 for bf16 (a group's kept-key list is held
- * on chip); Nq, Nkv <= 2^24; Nkv*d*4 < 2^31 (one head's K or V is
- * addressed with 32-bit byte offsets); B*H*max(Nq,Nkv)*d < 2^40.  Others
- * return MCS_ERR_UNSUPPORTED or MCS_ERR_INVALID_ARG before any launch. */
+ * 1 <= k <= Nkv; Nq, Nkv <= 2^24; Nkv*d*4 < 2^31 (one head's K or V is
+ * addressed with 32-bit byte offsets); B*H*max(Nq,Nkv)*d < 2^40; r_dtype
+ * MCS_BF16 only with dtype MCS_BF16.  Others return MCS_ERR_UNSUPPORTED or
+ * MCS_ERR_INVALID_ARG before any launch.  A zero-initialised struct with the
+ * sizes filled in selects the defaults (float32 data and residual). */
 typedef struct mcs_problem {
   int32_t B, H;         /* batch, heads                                        */
   int32_t Nq, Nkv;      /* query and key/value tokens per head (Nq may be 0)   */
@@ -78,6 +79,10 @@ typedef struct mcs_problem {
   int32_t q_offset;     /* position of query 0 in the KV sequence (>= 0)      */
   int32_t pddp_iters;   /* power-iteration steps per PDDP split (0..1024)      */
   int32_t dtype;        /* mcs_dtype of Q, K, V, O                             */
+  int32_t r_dtype;      /* mcs_dtype of the residual R: MCS_F32 (0, default),  */
+                        /* the difference of the float32 outputs stored whole; */
+                        /* MCS_BF16 (bf16 problems only) rounds it once more   */
+                        /* and halves its bytes                                */
 } mcs_problem;
 
 /* Bytes of workspace mcs_group (kind MCS_WS_GROUP), mcs_anchor
@@ -106,9 +111,11 @@ mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes,
 mcs_status mcs_group(const mcs_problem* p, const void* Q, int32_t* perm, void* ws, size_t ws_bytes,
                      void* stream);
 
-/* Exact (dense) softmax attention, the output MC-Sparse approximates and the
- * speed comparator: O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j over the
- * visible keys.
+/* Exact (dense) softmax attention over all 3D tokens, whose quadratic cost
+ * is the bottleneck the method removes (MC-Sparse review, section 2
+ * "Motivation"; FrameDiT summary, gist.science, "1. 연구 배경"), the output
+ * MC-Sparse approximates and the speed comparator:
+ * O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j over the visible keys.
  *   O   [B,H,Nq,d] dtype, written.
  *   lse [B,H,Nq] float32 or NULL: natural-log normaliser log sum_j exp(...)
  *       of each row (-inf for a row with no visible key, whose O is 0). */
@@ -127,8 +134,9 @@ mcs_status mcs_dense_attn(const mcs_problem* p, const void* Q, const void* K, co
  *   perm [B,H,Nq] int32, read (a valid grouping; not checked on the device).
  *   O    [B,H,Nq,d] dtype, written with O_full (rounded to dtype).
  *   idx  [B,H,c,k] int32, written: each group's selected key indices, ascending.
- *   R    [B,H,Nq,d] dtype, written (original token order): O_full - O_sparse
- *        formed in float32 from the unrounded O_full, rounded once to dtype.
+ *   R    [B,H,Nq,d] r_dtype, written (original token order): O_full - O_sparse
+ *        formed in float32 from the unrounded O_full (float32 by default;
+ *        rounded once to bf16 when r_dtype is MCS_BF16).
  *   ws   workspace of at least the minimum mcs_workspace_size(MCS_WS_ANCHOR). */
 mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const void* V,
                       const int32_t* perm, void* O, int32_t* idx, void* R, void* ws, size_t ws_bytes,
@@ -140,8 +148,8 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
  *   O_i = sum_{j in S_g(i), visible} softmax_j(scale*<q_i,k_j>) v_j + R_i.
  *   perm, idx from the anchor (perm must be a permutation of [0,Nq) and idx
  *   values in [0,Nkv); not checked on the device).
- *   R    [B,H,Nq,d] dtype from the anchor, or NULL for plain sparse attention;
- *        added in float32, the sum rounded once to dtype.
+ *   R    [B,H,Nq,d] r_dtype from the anchor, or NULL for plain sparse
+ *        attention; added in float32, the sum rounded once to dtype.
  *   O    [B,H,Nq,d] dtype, written (may not alias Q, K, V or R). */
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,
                            const int32_t* perm, const int32_t* idx, const void* R, void* O,
@@ -181,7 +189,9 @@ mcs_status mcs_block_select(const mcs_problem* p, const void* Q, const void* K, 
  *   rows   [n_rows] int32 device memory: token indices in [0,Nq), the same
  *          for every head (clamped into range on the device).
  *   n_rows 1..128.
- *   drift  [B,H] float32 device memory, written.
+ *   drift  [B*H + 1] float32 device memory, written: drift[b*H + h] for each
+ *          head, then drift[B*H] = the largest of them (NaN if any is NaN),
+ *          the value an anchor schedule compares with its threshold.
  *   ws     workspace of at least mcs_workspace_size(MCS_WS_DRIFT) bytes. */
 mcs_status mcs_residual_drift(const mcs_problem* p, const void* Q, const void* K, const void* V, const void* O,
                               const int32_t* rows, int32_t n_rows, float* drift, void* ws, size_t ws_bytes,

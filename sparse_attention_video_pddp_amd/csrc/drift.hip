@@ -229,19 +229,36 @@ __global__ __launch_bounds__(256) void drift_combine_kernel(DriftParams p) {
 
 // One wave per head: lane i adds rows i, i + 64, ... in order, then a fixed
 // butterfly over the lanes.
-__global__ __launch_bounds__(64) void drift_final_kernel(DriftParams p) {
-  const int bh = blockIdx.x, l = threadIdx.x;
-  float a = 0.f, b = 0.f;
-  for (int r = l; r < p.n_rows; r += 64) {
-    a += p.perr[2 * ((size_t)bh * p.n_rows + r)];
-    b += p.perr[2 * ((size_t)bh * p.n_rows + r) + 1];
-  }
+// One workgroup for all heads: wave w takes heads w, w + 16, ...; then the
+// largest drift over the heads (NaN if any is NaN) goes to drift[BH].
+__global__ __launch_bounds__(1024) void drift_final_kernel(DriftParams p, int BH) {
+  __shared__ float s_max[16];
+  const int w = wave_id(), l = lane_id();
+  const float qnan = __builtin_nanf("");
+  auto mx2 = [&](float x, float y) { return (x != x || y != y) ? qnan : fmaxf(x, y); };
+  float mx = 0.f;
+  for (int bh = w; bh < BH; bh += 16) {
+    float a = 0.f, b = 0.f;
+    for (int r = l; r < p.n_rows; r += 64) {
+      a += p.perr[2 * ((size_t)bh * p.n_rows + r)];
+      b += p.perr[2 * ((size_t)bh * p.n_rows + r) + 1];
+    }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    a += __shfl_xor(a, o, 64);
-    b += __shfl_xor(b, o, 64);
+    for (int o = 32; o >= 1; o >>= 1) {
+      a += __shfl_xor(a, o, 64);
+      b += __shfl_xor(b, o, 64);
+    }
+    const float dr = b > 0.f ? sqrtf(a / b) : 0.f;
+    if (l == 0) p.drift[bh] = dr;
+    mx = mx2(mx, dr);
   }
-  if (l == 0) p.drift[bh] = b > 0.f ? sqrtf(a / b) : 0.f;
+  if (l == 0) s_max[w] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int i = 0; i < 16; ++i) m = mx2(m, s_max[i]);
+    p.drift[BH] = m;
+  }
 }
 
 void drift_split(const Shape& s, int& nsplit, int& tps) {
@@ -283,7 +300,7 @@ hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K,
   else if (bf16) hipLaunchKernelGGL((drift_combine_kernel<__bf16, 64>), gcomb, dim3(256), 0, st, p);
   else if (s.d == 128) hipLaunchKernelGGL((drift_combine_kernel<float, 128>), gcomb, dim3(256), 0, st, p);
   else hipLaunchKernelGGL((drift_combine_kernel<float, 64>), gcomb, dim3(256), 0, st, p);
-  hipLaunchKernelGGL(drift_final_kernel, dim3(s.BH), dim3(64), 0, st, p);
+  hipLaunchKernelGGL(drift_final_kernel, dim3(1), dim3(1024), 0, st, p, s.BH);
   return hipGetLastError();
 }
 

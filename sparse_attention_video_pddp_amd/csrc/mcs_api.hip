@@ -37,6 +37,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Checked {
   mcs::Shape s;
   bool bf16;
+  bool r_f32;  // the residual is float32
   bool empty;
 };
 
@@ -63,9 +64,9 @@ mcs_status check_problem(const mcs_problem* p, Checked& out) {
   const long long bh = (long long)p->B * p->H;
   const long long nmax = p->Nq > p->Nkv ? p->Nq : p->Nkv;
   if (bh * nmax * p->d >= (1LL << 40)) return fail(MCS_ERR_UNSUPPORTED, "tensor sizes exceed 2^40 elements");
-  // the gathered attention keeps a group's key list in LDS next to its K/V ring
-  if (p->dtype == MCS_BF16 && p->k > mcs::kMaxKeysPerGroup)
-    return fail(MCS_ERR_UNSUPPORTED, "k=%d exceeds %d kept keys per group", p->k, mcs::kMaxKeysPerGroup);
+  if (p->r_dtype != MCS_F32 && p->r_dtype != MCS_BF16) return fail(MCS_ERR_UNSUPPORTED, "r_dtype=%d", p->r_dtype);
+  if (p->r_dtype == MCS_BF16 && p->dtype != MCS_BF16)
+    return fail(MCS_ERR_UNSUPPORTED, "a bf16 residual needs bf16 inputs (dtype=%d)", p->dtype);
   // K and V rows of one head are addressed with 32-bit byte offsets (buffer loads)
   if ((long long)p->Nkv * p->d * 4 > 0x7fffffffLL)
     return fail(MCS_ERR_UNSUPPORTED, "Nkv=%d: one head's K or V exceeds 2^31 bytes", p->Nkv);
@@ -73,6 +74,7 @@ mcs_status check_problem(const mcs_problem* p, Checked& out) {
   out.s = mcs::Shape{(int)bh,  p->Nq, p->Nkv, p->d, p->group_size, p->k, c, p->scale, p->causal_block,
                      p->q_offset, p->pddp_iters};
   out.bf16 = p->dtype == MCS_BF16;
+  out.r_f32 = p->r_dtype == MCS_F32;
   out.empty = bh == 0 || p->Nq == 0;
   return MCS_OK;
 }
@@ -229,7 +231,7 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
     e = mcs::launch_topk(c.s, bh0, nbh, mass, idx, st);
     if (e != hipSuccess) return hip_status(e, "mcs_anchor (top-k)");
   }
-  e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, ofull, R, nullptr, true, st)
+  e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, ofull, R, c.r_f32, nullptr, true, st)
              : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, (float*)R, nullptr, true, st);
   return hip_status(e, "mcs_anchor (sparse)");
 }
@@ -282,7 +284,7 @@ mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, c
   if (O == Q || O == K || O == V || O == R)
     return fail(MCS_ERR_INVALID_ARG, "O aliases an input");
   const hipStream_t st = (hipStream_t)stream;
-  const hipError_t e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, nullptr, (void*)R, O, false, st)
+  const hipError_t e = c.bf16 ? mcs::launch_sparse_bf16(c.s, Q, K, V, perm, idx, nullptr, (void*)R, c.r_f32, O, false, st)
                               : mcs::launch_sparse_f32(c.s, Q, K, V, perm, idx, (float*)R, O, false, st);
   return hip_status(e, "mcs_sparse_attn");
 }

@@ -6,10 +6,6 @@
 
 namespace mcs {
 
-// Largest k the bf16 gathered attention supports (its per-group key list
-// lives in LDS beside the K/V tile ring).
-constexpr int kMaxKeysPerGroup = 28672;
-
 // Validated problem, flattened for the launchers.
 struct Shape {
   int BH;        // B * H
@@ -35,11 +31,12 @@ hipError_t launch_mass_f32(const Shape& s, int bh0, int nbh, const void* Q, cons
 // Top-k per group row of `mass` (heads [bh0, bh0+nbh)), written to idx[bh][g][k] ascending.
 hipError_t launch_topk(const Shape& s, int bh0, int nbh, const float* mass, int32_t* idx, hipStream_t st);
 
-// Gathered sparse attention, bf16.  anchor: R <- bf16(Ofull - O_sparse)
-// (Ofull: the float32 dense output).  reuse: O <- O_sparse + R (R may be null).
+// Gathered sparse attention, bf16 inputs.  anchor: R <- Ofull - O_sparse
+// (Ofull: the float32 dense output), stored as float32 (r_f32) or rounded to
+// bf16.  reuse: O <- O_sparse + R (R may be null).
 hipError_t launch_sparse_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                              const int32_t* perm, const int32_t* idx, const float* Ofull, void* R, void* O,
-                              bool anchor, hipStream_t st);
+                              const int32_t* perm, const int32_t* idx, const float* Ofull, void* R, bool r_f32,
+                              void* O, bool anchor, hipStream_t st);
 // float32: anchor: R <- R - O_sparse (R holds O_full on entry); reuse as above.
 hipError_t launch_sparse_f32(const Shape& s, const void* Q, const void* K, const void* V,
                              const int32_t* perm, const int32_t* idx, float* R, void* O, bool anchor,
@@ -64,7 +61,8 @@ hipError_t launch_block_select(const Shape& s, bool bf16, const void* Q, const v
                                int32_t* idx, void* ws, hipStream_t st);
 
 // Residual-drift check: exact attention of at most kMaxDriftRows sampled
-// query rows per head, split over at most kMaxDriftSplits key ranges.
+// query rows per head, split over at most kMaxDriftSplits key ranges;
+// drift[BH] receives the largest per-head value.
 constexpr int kMaxDriftRows = 128;
 constexpr int kMaxDriftSplits = 64;
 size_t drift_workspace_bytes(const Shape& s);

@@ -29,7 +29,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32),
                 ("Nkv", ctypes.c_int32), ("d", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("scale", ctypes.c_float), ("causal_block", ctypes.c_int32),
-                ("q_offset", ctypes.c_int32), ("pddp_iters", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("q_offset", ctypes.c_int32), ("pddp_iters", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("r_dtype", ctypes.c_int32)]
 
     def __repr__(self) -> str:
         return "Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -88,16 +89,22 @@ def _check(status: int) -> None:
         raise MCSError(status, lib().mcs_last_error().decode())
 
 
+_DTYPES = {"f32": MCS_F32, "bf16": MCS_BF16}
+
+
 def problem(B: int, H: int, Nq: int, Nkv: int, d: int, group_size: int, k: int, scale: Optional[float] = None,
-            causal_block: int = 0, q_offset: int = 0, pddp_iters: int = 32, dtype: str = "bf16") -> Problem:
+            causal_block: int = 0, q_offset: int = 0, pddp_iters: int = 32, dtype: str = "bf16",
+            r_dtype: str = "f32") -> Problem:
+    """Problem description; the residual R is float32 unless r_dtype="bf16"
+    (bf16 problems only)."""
     return Problem(B, H, Nq, Nkv, d, group_size, k, 1.0 / math.sqrt(d) if scale is None else scale,
-                   causal_block, q_offset, pddp_iters, {"f32": MCS_F32, "bf16": MCS_BF16}[dtype])
+                   causal_block, q_offset, pddp_iters, _DTYPES[dtype], _DTYPES[r_dtype])
 
 
-def problem_for(w) -> Problem:
+def problem_for(w, r_dtype: str = "f32") -> Problem:
     """Problem of a synthetic workload (``synth.Workload``)."""
     return problem(w.B, w.H, w.Nq, w.Nkv, w.d, w.group_size, w.k, w.scale, w.causal_block, w.q_offset,
-                   w.pddp_iters, w.dtype)
+                   w.pddp_iters, w.dtype, r_dtype)
 
 
 def _ptr(x) -> Optional[int]:
@@ -115,6 +122,17 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _torch_stream(stream):
+    """The torch stream object for a ``stream`` argument (None: the current
+    stream; an int: a raw hipStream_t handle)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
 
 
 def workspace_size(p: Problem, kind: int) -> Tuple[int, int]:
@@ -152,6 +170,9 @@ def block_select(p: Problem, Q, K, perm, idx, ws, ws_bytes: Optional[int] = None
 
 def residual_drift(p: Problem, Q, K, V, O, rows, drift, ws, n_rows: Optional[int] = None,
                    ws_bytes: Optional[int] = None, stream=None) -> None:
+    """drift: B*H + 1 float32 values, the per-head drifts then their maximum."""
+    if hasattr(drift, "numel") and drift.numel() < p.B * p.H + 1:
+        raise ValueError(f"drift holds {drift.numel()} values; B*H + 1 = {p.B * p.H + 1} are written")
     n = rows.numel() if n_rows is None else n_rows
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib().mcs_residual_drift(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(rows), n,
@@ -171,7 +192,8 @@ class MCSparseAttention:
         BH = p.B * p.H
         self.perm = torch.empty((p.B, p.H, p.Nq), dtype=torch.int32, device=device)
         self.idx = torch.empty((p.B, p.H, p.n_groups, p.k), dtype=torch.int32, device=device)
-        self.R = torch.empty((p.B, p.H, p.Nq, p.d), dtype=dt, device=device)  # residual in the input dtype
+        rdt = torch.bfloat16 if p.r_dtype == MCS_BF16 else torch.float32
+        self.R = torch.empty((p.B, p.H, p.Nq, p.d), dtype=rdt, device=device)  # float32 unless asked for bf16
         self.O = torch.empty((p.B, p.H, p.Nq, p.d), dtype=dt, device=device)
         g, _ = workspace_size(p, MCS_WS_GROUP)
         a, _ = workspace_size(p, MCS_WS_ANCHOR)
@@ -226,7 +248,7 @@ class AdaptiveAnchoring:
     ``max_period`` steps have passed since the last anchor (0: no limit).
     ``step(Q, K, V)`` returns O; ``history`` records (is_anchor, drift) per
     step.  Reading the drift back costs one host synchronisation per reuse
-    step."""
+    step; the read is ordered after the check on the stream it ran on."""
 
     def __init__(self, layer: MCSparseAttention, threshold: float, max_period: int = 0, n_rows: int = 64,
                  device="cuda"):
@@ -234,7 +256,7 @@ class AdaptiveAnchoring:
         self.layer, self.threshold, self.max_period = layer, threshold, max_period
         p = layer.p
         self.rows = torch.tensor(drift_rows(p.Nq, n_rows), dtype=torch.int32, device=device)
-        self.drift = torch.zeros((p.B, p.H), dtype=torch.float32, device=device)
+        self.drift = torch.zeros(p.B * p.H + 1, dtype=torch.float32, device=device)  # per head, then the max
         b, _ = workspace_size(p, MCS_WS_DRIFT)
         self.ws = torch.empty(max(b, 1), dtype=torch.uint8, device=device)
         self.anchor_next = True
@@ -255,8 +277,9 @@ class AdaptiveAnchoring:
             return O
         O = self.layer.step(Q, K, V, False, stream=stream)
         residual_drift(self.layer.p, Q, K, V, O, self.rows, self.drift, self.ws, stream=stream)
-        vals = self.drift.cpu().flatten().tolist()  # B*H floats read back; the max on the host
-        d = math.nan if any(v != v for v in vals) else max(vals, default=0.0)
+        import torch
+        with torch.cuda.stream(_torch_stream(stream)):
+            d = self.drift[-1].item()  # the largest drift over the heads, computed by the library
         self.since += 1
         self.anchor_next = self.decide(d, self.threshold, self.since, self.max_period)
         self.history.append((False, d))
@@ -279,7 +302,8 @@ class ChunkedCausalStream:
     fresh ``MCSparseAttention`` in ``begin_chunk``); the anchor schedule inside
     a chunk is the caller's.  ``step`` writes the chunk's current K/V rows
     into the cache (or the caller fills ``kv_rows()`` in place) and runs the
-    step."""
+    step, all on ``stream``, which first waits for the current stream (where
+    the caller made the chunk's rows)."""
 
     def __init__(self, B: int, H: int, d: int, frame_tokens: int, frames_per_chunk: int, n_chunks: int,
                  group_size: int, k: int, scale: Optional[float] = None, dtype: str = "bf16",
@@ -322,8 +346,14 @@ class ChunkedCausalStream:
     def step(self, Q, K_chunk=None, V_chunk=None, is_anchor: bool = False, stream=None):
         if self.layer is None:
             raise RuntimeError("begin_chunk() first")
+        import torch
+        ts = _torch_stream(stream)
+        cur = torch.cuda.current_stream()
+        if ts != cur:
+            ts.wait_stream(cur)
         if K_chunk is not None:
             k, v = self.kv_rows()
-            k.copy_(K_chunk)
-            v.copy_(V_chunk)
-        return self.layer.step(Q, self.K, self.V, is_anchor, stream=stream)
+            with torch.cuda.stream(ts):
+                k.copy_(K_chunk)
+                v.copy_(V_chunk)
+        return self.layer.step(Q, self.K, self.V, is_anchor, stream=ts)

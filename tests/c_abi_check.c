@@ -22,6 +22,8 @@ int main(void) {
   memset(&p, 0, sizeof p);
   p.B = 1; p.H = 12; p.Nq = 32760; p.Nkv = 32760; p.d = 128; p.group_size = 64; p.k = 1638;
   p.scale = 0.08838834764831845f; p.pddp_iters = 32; p.dtype = MCS_BF16;
+  CHECK(p.r_dtype == MCS_F32); /* zero-initialised: float32 residual */
+  CHECK(sizeof(mcs_problem) == 13 * sizeof(int32_t));
 
   CHECK(mcs_version() > 0);
   CHECK(strcmp(mcs_status_string(MCS_OK), "MCS_OK") == 0);
@@ -38,6 +40,15 @@ int main(void) {
   CHECK(s == MCS_ERR_UNSUPPORTED);
   CHECK(strlen(mcs_last_error()) > 0);
   p.d = 128;
+
+  /* a bf16 residual needs bf16 inputs */
+  p.dtype = MCS_F32; p.r_dtype = MCS_BF16;
+  s = mcs_workspace_size(&p, MCS_WS_ANCHOR, &bytes, &min_bytes);
+  CHECK(s == MCS_ERR_UNSUPPORTED);
+  p.dtype = MCS_BF16;
+  s = mcs_workspace_size(&p, MCS_WS_ANCHOR, &bytes, &min_bytes);
+  CHECK(s == MCS_OK);
+  p.r_dtype = MCS_F32;
 
   /* a NULL pointer is refused before any launch */
   s = mcs_dense_attn(&p, NULL, NULL, NULL, NULL, NULL, NULL);

@@ -55,7 +55,7 @@ def base(**kw):
     (dict(pddp_iters=5000), mcs.MCS_ERR_INVALID_ARG),
     (dict(B=300, H=300), mcs.MCS_ERR_UNSUPPORTED),
     (dict(Nkv=1 << 22, k=60), mcs.MCS_ERR_UNSUPPORTED),   # one head's K > 2^31 bytes (32-bit offsets)
-    (dict(Nkv=40000, k=28673), mcs.MCS_ERR_UNSUPPORTED),  # kept-key list larger than the on-chip table
+    (dict(dtype="f32", r_dtype="bf16"), mcs.MCS_ERR_UNSUPPORTED),  # a bf16 residual needs bf16 inputs
 ])
 def test_bad_problem_is_rejected_before_launch(kw, code):
     p = base(**kw)
@@ -72,6 +72,22 @@ def test_bad_dtype_rejected():
     with pytest.raises(mcs.MCSError) as e:
         mcs.sparse_attn(p, 16, 16, 16, 16, 16, None, 32, stream=0)
     assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
+    p = base()
+    p.r_dtype = 5
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.sparse_attn(p, 16, 16, 16, 16, 16, None, 32, stream=0)
+    assert e.value.status == mcs.MCS_ERR_UNSUPPORTED and "r_dtype" in str(e.value)
+
+
+def test_residual_dtype_defaults_to_float32():
+    """A problem with r_dtype left at zero keeps R in float32; every kept-key
+    count up to Nkv is accepted (no on-chip table limits k)."""
+    p = base()
+    assert p.r_dtype == mcs.MCS_F32 == 0
+    assert base(r_dtype="bf16").r_dtype == mcs.MCS_BF16
+    for k in (1, 28673, 40000):
+        mcs.workspace_size(base(Nkv=40000, k=k), mcs.MCS_WS_ANCHOR)
+    assert ctypes.sizeof(mcs.Problem) == 13 * 4
 
 
 def test_null_and_misaligned_pointers_rejected():

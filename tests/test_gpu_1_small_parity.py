@@ -75,6 +75,22 @@ def test_small_workload_parity(cuda, name):
         assert_reports(reps, f"{name} head {bh}")
 
 
+@pytest.mark.parametrize("name", ["bidir_small", "causal_small", "large_small", "stress_small", "d64_g64",
+                                  "offset_d128_g64"])
+def test_small_workload_parity_bf16_residual(cuda, name):
+    """The same staged parity with the residual stored in bf16 (r_dtype
+    MCS_BF16, one more rounding of R): every head, group and row."""
+    from tests.gpu_runner import log, run_anchor_reuse
+    w = SMALL[name]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    cases = run_anchor_reuse(w, heads, r_dtype="bf16")
+    for bh, case in cases.items():
+        reps = check_head(case, w.group_size, w.k, w.scale, w.causal_block, w.q_offset, w.pddp_iters)
+        for r in reps:
+            log(f"  {name} (bf16 R) head {bh}: {r}")
+        assert_reports(reps, f"{name} (bf16 R) head {bh}")
+
+
 def test_dense_attn_matches_oracle_with_lse(cuda):
     import torch
     from oracle.mcs_oracle import dense_attention
@@ -123,6 +139,38 @@ def test_full_keep_sparse_equals_dense(cuda):
         d = (Os.float() - Od.float()).abs()
         assert d.max().item() <= 1e-2 * vmax and d.mean().item() <= 1e-3 * vmax, (base, d.max().item())
         assert st.R.abs().max().item() <= 1e-2 * vmax
+
+
+@pytest.mark.parametrize("name", ["bidir5", "causal"])
+def test_full_keep_at_full_length(cuda, name):
+    """keep 100% at the benchmark's length (k = Nkv = 32760 kept keys per
+    group, two heads): every group selects every key, the sparse kernel
+    without R reproduces the dense kernel and R vanishes to rounding.  The
+    frame-causal query chunk finds each query's visible prefix of a list far
+    longer than the kernel's LDS scratch (its search runs in global memory)."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    from tests.gpu_runner import log
+    w = synth.get(name).with_(H=2, keep_permille=1000)
+    assert w.k == w.Nkv == 32760
+    p = mcs.problem_for(w)
+    (Q, K, V), _ = device_inputs(w, 0)
+    st = _state(w)
+    st.step(Q, K, V, True)
+    full = torch.arange(w.Nkv, dtype=torch.int32, device="cuda")
+    assert torch.equal(st.idx[0, 0, 0], full) and torch.equal(st.idx[0, 1, -1], full)
+    Od = torch.empty_like(Q)
+    mcs.dense_attn(p, Q, K, V, Od)
+    Os = torch.empty_like(Q)
+    mcs.sparse_attn(p, Q, K, V, st.perm, st.idx, None, Os)
+    torch.cuda.synchronize()
+    vmax = V.float().abs().max().item()
+    d = (Os.float() - Od.float()).abs()
+    log(f"  {name} keep 100%: max|sparse - dense| {d.max().item():.3e} mean {d.mean().item():.3e} "
+        f"max|R| {st.R.abs().max().item():.3e} (vmax {vmax:.3f})")
+    assert d.max().item() <= 1e-2 * vmax and d.mean().item() <= 1e-3 * vmax
+    assert st.R.abs().max().item() <= 1e-2 * vmax
 
 
 def test_zero_drift_reuse_returns_anchor_output(cuda):

@@ -31,11 +31,14 @@ def _drift(p, Q, K, V, O, rows):
     import torch
     from sparse_attention_video_pddp_amd import mcs
     rows_t = torch.tensor(rows, dtype=torch.int32, device="cuda")
-    drift = torch.full((p.B, p.H), -1.0, dtype=torch.float32, device="cuda")
+    drift = torch.full((p.B * p.H + 1,), -1.0, dtype=torch.float32, device="cuda")
     ws = torch.empty(max(mcs.workspace_size(p, mcs.MCS_WS_DRIFT)[0], 1), dtype=torch.uint8, device="cuda")
     mcs.residual_drift(p, Q, K, V, O, rows_t, drift, ws)
     torch.cuda.synchronize()
-    return drift.cpu().numpy()
+    d = drift.cpu().numpy()
+    # the last value is the largest per-head drift, formed by the library
+    assert d[-1] == d[:-1].max(), d
+    return d[:-1].reshape(p.B, p.H)
 
 
 def _tol(want):
@@ -144,3 +147,36 @@ def test_adaptive_schedule_follows_the_drift(cuda):
     for x in steps:
         cap.step(*x)
     assert [a for a, _ in cap.history] == [True, False, True, False, True, False]
+
+
+def test_adaptive_schedule_on_a_side_stream(cuda):
+    """AdaptiveAnchoring handed a side stream without a stream context: the
+    library's check runs on that stream and the binding reads the largest
+    drift back on it too, so the drifts, anchor decisions and outputs equal
+    those of the same schedule on the current stream bit for bit."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    w = SMALL["large_small"]
+    p = mcs.problem_for(w)
+    steps = [device_inputs(w, s)[0] for s in range(5)]
+    torch.cuda.synchronize()
+
+    def run(stream, threshold):
+        ad = mcs.AdaptiveAnchoring(mcs.MCSparseAttention(p), threshold=threshold)
+        outs = []
+        for x in steps:
+            O = ad.step(*x, stream=stream)
+            (stream or torch.cuda.current_stream()).synchronize()
+            outs.append(O.clone())
+        return ad.history, outs
+
+    hist0, _ = run(None, float("inf"))
+    d = [dr for a, dr in hist0 if not a]
+    assert len(d) == 4 and all(np.isfinite(d)) and max(d) > min(d)
+    thr = float(np.median(d))
+    ref_hist, ref_out = run(None, thr)
+    side_hist, side_out = run(torch.cuda.Stream(), thr)
+    assert side_hist == ref_hist and any(a for a, _ in ref_hist[1:])
+    for a, b in zip(ref_out, side_out):
+        assert torch.equal(a, b)

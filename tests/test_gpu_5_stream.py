@@ -85,3 +85,39 @@ def test_chunked_causal_stream_parity(cuda):
     assert np.array_equal(st.K[0].float().cpu().numpy(), cache_k)
     with pytest.raises(RuntimeError):
         st.begin_chunk()
+
+
+def test_chunked_stream_on_a_side_stream(cuda):
+    """ChunkedCausalStream handed a side stream without a stream context: the
+    chunk's K/V rows are copied into the cache on that stream after it waits
+    for the current one (where they were made), so every output and the cache
+    equal those of the current stream bit for bit."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import _to_tensor
+    ft = HGT * WID
+    n_chunks = T // FPC
+
+    def run(stream):
+        w0 = BASE.with_(q_frames=(0, FPC))
+        st = mcs.ChunkedCausalStream(w0.B, w0.H, w0.d, ft, FPC, n_chunks, w0.group_size, w0.k, w0.scale,
+                                     w0.dtype, w0.pddp_iters)
+        outs = []
+        for c in range(2):
+            wc = BASE.with_(q_frames=(c * FPC, (c + 1) * FPC))
+            st.begin_chunk()
+            r = st.rows()
+            for s in range(2):
+                hs = [synth.head_inputs(wc, 0, h, s) for h in range(wc.H)]
+                dev = [torch.stack([_to_tensor(x[i] if i == 0 else x[i][r], wc.dtype) for x in hs])[None]
+                       .to("cuda") for i in range(3)]
+                O = st.step(dev[0], dev[1], dev[2], is_anchor=(s == 0), stream=stream)
+                (stream or torch.cuda.current_stream()).synchronize()
+                outs.append(O.clone())
+        return outs, st.K.clone(), st.V.clone()
+
+    ref = run(None)
+    side = run(torch.cuda.Stream())
+    for a, b in zip(ref[0], side[0]):
+        assert torch.equal(a, b)
+    assert torch.equal(ref[1], side[1]) and torch.equal(ref[2], side[2])

@@ -109,12 +109,13 @@ def _foreign_cache_case(kv_grid, k, cfg_id, label):
     assert_reports(reps, label)
 
 
-def test_largest_kept_key_count(cuda):
-    """The largest supported selection: k = 28672 kept keys per group (the
-    bf16 path's on-chip index table is full) out of a 30240-key cache
-    (472.5 key tiles: a ragged tail), two groups of 64 queries.  The boundary
-    of the top-k then lies deep in the low-mass tail, where near-ties are
-    common; tests/parity.py validates the GPU's choice there."""
+def test_large_kept_key_count(cuda):
+    """A large selection: k = 28672 kept keys per group out of a 30240-key
+    cache (472.5 key tiles: a ragged tail; the gathered kernel streams the
+    offsets of 896 tiles through its eight-tile ring), two groups of 64
+    queries.  The boundary of the top-k then lies deep in the low-mass tail,
+    where near-ties are common; tests/parity.py validates the GPU's choice
+    there."""
     _foreign_cache_case((12, 40, 63), 28672, 98, "k = 28672 of 30240 keys")
 
 
