@@ -197,6 +197,25 @@ mcs_status mcs_residual_drift(const mcs_problem* p, const void* Q, const void* K
                               const int32_t* rows, int32_t n_rows, float* drift, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* mcs_residual_drift without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results as
+ * mcs_residual_drift; its scratch is a static device array of 64 MiB (one
+ * copy per GPU, held until the process ends), whose address on the current
+ * device is looked up on the first call there.  The call allocates nothing.
+ *   Scratch needed: 4*B*H*n_rows*(nsplit*(d + 2) + 2) bytes with nsplit =
+ *   ceil(ceil(Nkv/64) / max(8, ceil(ceil(Nkv/64)/64))) key ranges (at most
+ *   64); a problem needing more than 64 MiB returns MCS_ERR_WORKSPACE before
+ *   any launch (32760 keys, 12 heads, d = 128 fit all 128 rows; 75600 keys,
+ *   40 heads, d = 128 up to 51).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (other streams or threads) race and must be serialised by the
+ *   caller.  Nothing needs clearing between calls: every scratch value a
+ *   call reads is first written by that call. */
+mcs_status mcs_residual_drift_noalloc(const mcs_problem* p, const void* Q, const void* K, const void* V,
+                                      const void* O, const int32_t* rows, int32_t n_rows, float* drift,
+                                      void* stream);
+
 /* Static description of a status code. */
 const char* mcs_status_string(mcs_status s);
 

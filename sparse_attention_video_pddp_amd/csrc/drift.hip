@@ -29,8 +29,8 @@ constexpr int kDriftTK = 64;  // keys per tile
 struct DriftParams {
   const void *Q, *K, *V, *O;
   const int32_t* rows;
-  float* pm;     // [BH][nsplit][kMaxDriftRows][2]: m (scaled log2), l
-  float* po;     // [BH][nsplit][kMaxDriftRows][d]: unnormalised output
+  float* pm;     // [BH][nsplit][n_rows][2]: m (scaled log2), l
+  float* po;     // [BH][nsplit][n_rows][d]: unnormalised output
   float* perr;   // [BH][n_rows][2]: squared error, squared norm
   float* drift;  // [BH]
   int Nq, Nkv, n_rows, nsplit, tps;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void rows_partial_bf16_kernel(DriftParams p) {
   }
   const float lt = half_sum(fc.l_run);
   if (!valid) return;
-  const size_t pr = ((size_t)bh * p.nsplit + sp) * kMaxDriftRows + r;
+  const size_t pr = ((size_t)bh * p.nsplit + sp) * p.n_rows + r;
   if (h == 0) {
     p.pm[2 * pr] = fc.m_run;
     p.pm[2 * pr + 1] = lt;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64) void rows_partial_f32_kernel(DriftParams p) {
   __syncthreads();
   float M = -kInf;
   for (int i = 0; i < 64; ++i) M = fmaxf(M, sm[i]);
-  const size_t pr = ((size_t)bh * p.nsplit + sp) * kMaxDriftRows + r;
+  const size_t pr = ((size_t)bh * p.nsplit + sp) * p.n_rows + r;
   if (l == 0) {
     float L = 0.f;
     for (int i = 0; i < 64; ++i)
@@ -184,16 +184,16 @@ __global__ __launch_bounds__(256) void drift_combine_kernel(DriftParams p) {
   __shared__ float s_L;
   __shared__ float red[2][D];
   const int bh = blockIdx.x / p.n_rows, r = blockIdx.x - bh * p.n_rows;
-  const size_t base = (size_t)bh * p.nsplit * kMaxDriftRows + r;  // (bh, split 0, r)
+  const size_t base = (size_t)bh * p.nsplit * p.n_rows + r;  // (bh, split 0, r)
   const int tid = threadIdx.x;
   if (tid < 64) {
     float M = -kInf;
-    for (int s = tid; s < p.nsplit; s += 64) M = fmaxf(M, p.pm[2 * (base + (size_t)s * kMaxDriftRows)]);
+    for (int s = tid; s < p.nsplit; s += 64) M = fmaxf(M, p.pm[2 * (base + (size_t)s * p.n_rows)]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float L = 0.f;
     for (int s = tid; s < p.nsplit; s += 64) {
-      const size_t pr = base + (size_t)s * kMaxDriftRows;
+      const size_t pr = base + (size_t)s * p.n_rows;
       const float ms = p.pm[2 * pr];
       const float wv = (ms == -kInf) ? 0.f : exp2f(ms - M);
       wgt[s] = wv;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void drift_combine_kernel(DriftParams p) {
   if (tid < D) {
     float acc = 0.f;
 #pragma unroll 8
-    for (int s = 0; s < p.nsplit; ++s) acc = fmaf(p.po[(base + (size_t)s * kMaxDriftRows) * D + tid], wgt[s], acc);
+    for (int s = 0; s < p.nsplit; ++s) acc = fmaf(p.po[(base + (size_t)s * p.n_rows) * D + tid], wgt[s], acc);
     const float L = s_L;
     const float ex = L > 0.f ? acc / L : 0.f;
     const float got = (float)((const T*)p.O)[((size_t)bh * p.Nq + sampled_row(p, r)) * D + tid];
@@ -227,10 +227,10 @@ __global__ __launch_bounds__(256) void drift_combine_kernel(DriftParams p) {
   }
 }
 
-// One wave per head: lane i adds rows i, i + 64, ... in order, then a fixed
-// butterfly over the lanes.
-// One workgroup for all heads: wave w takes heads w, w + 16, ...; then the
-// largest drift over the heads (NaN if any is NaN) goes to drift[BH].
+// One workgroup for all heads: wave w takes heads w, w + 16, ... (lane i
+// adds rows i, i + 64, ... in order, then a fixed butterfly over the lanes);
+// then the largest drift over the heads (NaN if any is NaN) goes to
+// drift[BH].
 __global__ __launch_bounds__(1024) void drift_final_kernel(DriftParams p, int BH) {
   __shared__ float s_max[16];
   const int w = wave_id(), l = lane_id();
@@ -269,10 +269,10 @@ void drift_split(const Shape& s, int& nsplit, int& tps) {
 
 }  // namespace
 
-size_t drift_workspace_bytes(const Shape& s) {
+size_t drift_workspace_bytes(const Shape& s, int n_rows) {
   int nsplit, tps;
   drift_split(s, nsplit, tps);
-  return (size_t)s.BH * ((size_t)nsplit * kMaxDriftRows * (2 + s.d) + kMaxDriftRows * 2) * 4;
+  return (size_t)s.BH * ((size_t)nsplit * n_rows * (2 + s.d) + (size_t)n_rows * 2) * 4;
 }
 
 hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K, const void* V, const void* O,
@@ -282,8 +282,8 @@ hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K,
   p.Nq = s.Nq; p.Nkv = s.Nkv; p.n_rows = n_rows;
   drift_split(s, p.nsplit, p.tps);
   p.pm = (float*)ws;
-  p.po = p.pm + (size_t)s.BH * p.nsplit * kMaxDriftRows * 2;
-  p.perr = p.po + (size_t)s.BH * p.nsplit * kMaxDriftRows * s.d;
+  p.po = p.pm + (size_t)s.BH * p.nsplit * n_rows * 2;
+  p.perr = p.po + (size_t)s.BH * p.nsplit * n_rows * s.d;
   p.c = s.scale * kLog2e; p.scale = s.scale;
   p.causal_block = s.causal_block; p.q_offset = s.q_offset;
   const dim3 gpart((unsigned)((long long)s.BH * p.nsplit));

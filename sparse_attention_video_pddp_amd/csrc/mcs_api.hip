@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "mcs.h"
@@ -128,6 +129,35 @@ mcs_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Scratch of mcs_residual_drift_noalloc: a fixed array in device memory, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in): its device address on the current GPU is looked up once with
+// hipGetSymbolAddress and kept per device.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mcs_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MCS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MCS_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MCS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MCS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,7 +193,7 @@ mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes,
   } else if (kind == MCS_WS_BLOCK) {
     need = need_min = c.empty ? 0 : mcs::block_workspace_bytes(c.s);
   } else if (kind == MCS_WS_DRIFT) {
-    need = need_min = c.empty ? 0 : mcs::drift_workspace_bytes(c.s);
+    need = need_min = c.empty ? 0 : mcs::drift_workspace_bytes(c.s, mcs::kMaxDriftRows);
   } else {
     return fail(MCS_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
   }
@@ -263,13 +293,34 @@ mcs_status mcs_residual_drift(const mcs_problem* p, const void* Q, const void* K
   if (n_rows < 1 || n_rows > mcs::kMaxDriftRows)
     return fail(MCS_ERR_INVALID_ARG, "n_rows=%d outside [1, %d]", n_rows, mcs::kMaxDriftRows);
   if (c.empty) return ok();
-  const size_t need = mcs::drift_workspace_bytes(c.s);
+  const size_t need = mcs::drift_workspace_bytes(c.s, n_rows);
   if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "drift workspace %zu < %zu bytes", ws_bytes, need);
   if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {O, "O", false},
                                  {rows, "rows", false}, {drift, "drift", false}, {ws, "ws", false}}))
     return s;
   return hip_status(mcs::launch_drift(c.s, c.bf16, Q, K, V, O, rows, n_rows, drift, ws, (hipStream_t)stream),
                     "mcs_residual_drift");
+}
+
+mcs_status mcs_residual_drift_noalloc(const mcs_problem* p, const void* Q, const void* K, const void* V,
+                                      const void* O, const int32_t* rows, int32_t n_rows, float* drift,
+                                      void* stream) {
+  Checked c;
+  if (mcs_status s = check_problem(p, c)) return s;
+  if (n_rows < 1 || n_rows > mcs::kMaxDriftRows)
+    return fail(MCS_ERR_INVALID_ARG, "n_rows=%d outside [1, %d]", n_rows, mcs::kMaxDriftRows);
+  if (c.empty) return ok();
+  const size_t need = mcs::drift_workspace_bytes(c.s, n_rows);
+  if (need > kNoallocScratchBytes)
+    return fail(MCS_ERR_WORKSPACE, "the check needs %zu bytes of scratch, more than the %zu of the static scratch",
+                need, kNoallocScratchBytes);
+  if (mcs_status s = check_ptrs({{Q, "Q", false}, {K, "K", false}, {V, "V", false}, {O, "O", false},
+                                 {rows, "rows", false}, {drift, "drift", false}}))
+    return s;
+  void* ws = nullptr;
+  if (mcs_status s = scratch_on_current_device(&ws)) return s;
+  return hip_status(mcs::launch_drift(c.s, c.bf16, Q, K, V, O, rows, n_rows, drift, ws, (hipStream_t)stream),
+                    "mcs_residual_drift_noalloc");
 }
 
 mcs_status mcs_sparse_attn(const mcs_problem* p, const void* Q, const void* K, const void* V,

@@ -65,7 +65,9 @@ hipError_t launch_block_select(const Shape& s, bool bf16, const void* Q, const v
 // drift[BH] receives the largest per-head value.
 constexpr int kMaxDriftRows = 128;
 constexpr int kMaxDriftSplits = 64;
-size_t drift_workspace_bytes(const Shape& s);
+// Scratch of a check over n_rows sampled rows (every value read is first
+// written by the same call: nothing needs clearing).
+size_t drift_workspace_bytes(const Shape& s, int n_rows);
 hipError_t launch_drift(const Shape& s, bool bf16, const void* Q, const void* K, const void* V, const void* O,
                         const int32_t* rows, int n_rows, float* drift, void* ws, hipStream_t st);
 

@@ -22,7 +22,8 @@ MCS_WS_GROUP, MCS_WS_ANCHOR, MCS_WS_BLOCK, MCS_WS_DRIFT = 0, 1, 2, 3
 MAX_DRIFT_ROWS = 128
 
 EXPORTED = ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
-            "mcs_block_select", "mcs_residual_drift", "mcs_status_string", "mcs_last_error", "mcs_version")
+            "mcs_block_select", "mcs_residual_drift", "mcs_residual_drift_noalloc", "mcs_status_string",
+            "mcs_last_error", "mcs_version")
 
 
 class Problem(ctypes.Structure):
@@ -72,8 +73,9 @@ def lib() -> ctypes.CDLL:
         L.mcs_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mcs_block_select.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.mcs_residual_drift.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, sz, vp]
+        L.mcs_residual_drift_noalloc.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp]
         for f in ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
-                  "mcs_block_select", "mcs_residual_drift"):
+                  "mcs_block_select", "mcs_residual_drift", "mcs_residual_drift_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.mcs_status_string.argtypes = [ctypes.c_int]
         L.mcs_status_string.restype = ctypes.c_char_p
@@ -177,6 +179,16 @@ def residual_drift(p: Problem, Q, K, V, O, rows, drift, ws, n_rows: Optional[int
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib().mcs_residual_drift(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(rows), n,
                                     _ptr(drift), _ptr(ws), nbytes, _stream(stream)))
+
+
+def residual_drift_noalloc(p: Problem, Q, K, V, O, rows, drift, n_rows: Optional[int] = None, stream=None) -> None:
+    """mcs_residual_drift without a workspace: the library's static scratch
+    (for callers that cannot allocate; calls overlapping on one GPU race)."""
+    if hasattr(drift, "numel") and drift.numel() < p.B * p.H + 1:
+        raise ValueError(f"drift holds {drift.numel()} values; B*H + 1 = {p.B * p.H + 1} are written")
+    n = rows.numel() if n_rows is None else n_rows
+    _check(lib().mcs_residual_drift_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(rows), n,
+                                            _ptr(drift), _stream(stream)))
 
 
 class MCSparseAttention:

@@ -159,10 +159,28 @@ def test_residual_drift_workspace_and_limits():
         with pytest.raises(mcs.MCSError) as e:
             mcs.residual_drift(p, 16, 16, 16, 16, 16, 32, 48, n_rows=n, ws_bytes=b, stream=0)
         assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "n_rows" in str(e.value)
-    with pytest.raises(mcs.MCSError) as e:
-        mcs.residual_drift(p, 16, 16, 16, 16, 16, 32, 48, n_rows=8, ws_bytes=b - 1, stream=0)
+    with pytest.raises(mcs.MCSError) as e:      # the workspace size is for the largest n_rows
+        mcs.residual_drift(p, 16, 16, 16, 16, 16, 32, 48, n_rows=128, ws_bytes=b - 1, stream=0)
+    assert e.value.status == mcs.MCS_ERR_WORKSPACE
+    with pytest.raises(mcs.MCSError) as e:      # fewer rows need less: 8/128 of it is not enough for 9
+        mcs.residual_drift(p, 16, 16, 16, 16, 16, 32, 48, n_rows=9, ws_bytes=b * 8 // 128, stream=0)
     assert e.value.status == mcs.MCS_ERR_WORKSPACE
     mcs.residual_drift(base(Nq=0), None, None, None, None, None, None, None, n_rows=8, ws_bytes=0, stream=0)
+
+
+def test_noalloc_drift_limits_on_the_host():
+    """The allocation-free check refuses, before touching any device, a
+    problem whose scratch exceeds its 64 MiB static array, and bad row counts;
+    an empty problem is a no-op."""
+    big = mcs.problem(1, 40, 75600, 75600, 128, 128, 2268, dtype="bf16")
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.residual_drift_noalloc(big, 16, 16, 16, 16, 16, 32, n_rows=128, stream=0)
+    assert e.value.status == mcs.MCS_ERR_WORKSPACE and "static scratch" in str(e.value)
+    for n in (0, 129):
+        with pytest.raises(mcs.MCSError) as e:
+            mcs.residual_drift_noalloc(base(), 16, 16, 16, 16, 16, 32, n_rows=n, stream=0)
+        assert e.value.status == mcs.MCS_ERR_INVALID_ARG
+    mcs.residual_drift_noalloc(base(Nq=0), None, None, None, None, None, None, n_rows=8, stream=0)
 
 
 def test_drift_rows_are_spread_and_bounded():
