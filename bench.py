@@ -421,10 +421,13 @@ def cpu_baseline(w, host0, host1, nheads: int, reuse_budget_s: float = 10.0):
 def stream_main(args) -> None:
     """Chunked-causal streaming at full size: the frame-causal workload's video
     (grid T x H x W, chunks of its query-chunk length) generated chunk by chunk
-    over a zero-initialised K/V cache of the whole video.  Inputs: the
-    workload's generator for the whole video at step 0 (queries of every
-    frame), then per step an extra drift of the current chunk's rows drawn on
-    the device (seeded).  Timed with HIP events per call, caches flushed."""
+    over a zero-initialised K/V cache of the whole video, once with each
+    anchor mode (two-pass: column-mass matrix then top-k; single-pass: each
+    group's mass kept on chip and selected in the same workgroup; both give
+    the same selections).  Inputs: the workload's generator for the whole
+    video at step 0 (queries of every frame), then per step an extra drift of
+    the current chunk's rows drawn on the device (seeded, the same for both
+    modes).  Timed with HIP events per call, caches flushed."""
     import torch
     from sparse_attention_video_pddp_amd import mcs, synth
     from sparse_attention_video_pddp_amd.workload import device_inputs
@@ -438,58 +441,71 @@ def stream_main(args) -> None:
     (Qa, Ka, Va), _ = device_inputs(full, 0)
     ft = Hg * Wg
     n_chunks = T // fpc
-    st = mcs.ChunkedCausalStream(full.B, full.H, full.d, ft, fpc, n_chunks, full.group_size, full.k, full.scale,
-                                 full.dtype, full.pddp_iters)
     A = base.anchor_every
     steps = max(A, 4)
-    # untimed: one anchor and one reuse step of a first chunk (first launches of every kernel)
-    warm = mcs.ChunkedCausalStream(full.B, full.H, full.d, ft, fpc, n_chunks, full.group_size, full.k,
-                                   full.scale, full.dtype, full.pddp_iters)
-    warm.begin_chunk()
-    wr = warm.rows()
-    for anchor in (True, False):
-        warm.step(Qa[:, :, wr], Ka[:, :, wr], Va[:, :, wr], anchor)
-    torch.cuda.synchronize()
-    del warm
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1234)
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    rec = []
-    for c in range(n_chunks):
-        st.begin_chunk()
-        r = st.rows()
-        Q, K, V = Qa[:, :, r].clone(), Ka[:, :, r].clone(), Va[:, :, r].clone()
-        for s in range(steps):
-            if s:
-                for X in (Q, K, V):
-                    X += (full.drift * torch.randn(X.shape, generator=gen, device=dev)).to(X.dtype)
-            anchor = s % A == 0
-            scratch.fill_(s & 255)
-            a, b = ev(), ev()
-            a.record(stream)
-            st.step(Q, K, V, anchor, stream=stream)
-            b.record(stream)
-            rec.append((c, anchor, a, b))
-    torch.cuda.synchronize()
-    per = {}
-    for c, anchor, a, b in rec:
-        per.setdefault(c, {"anchor_ms": [], "reuse_ms": []})["anchor_ms" if anchor else "reuse_ms"].append(
-            a.elapsed_time(b))
-    chunks = [{"chunk": c, "visible_keys": (c + 1) * st.chunk_tokens,
-               "anchor_ms": round(statistics.fmean(v["anchor_ms"]), 4),
-               "reuse_ms": round(statistics.fmean(v["reuse_ms"]), 4)} for c, v in sorted(per.items())]
-    total = sum(a.elapsed_time(b) for _, _, a, b in rec)
+
+    def run(mode):
+        mk = lambda: mcs.ChunkedCausalStream(full.B, full.H, full.d, ft, fpc, n_chunks, full.group_size,  # noqa
+                                             full.k, full.scale, full.dtype, full.pddp_iters, anchor_mode=mode)
+        # untimed: one anchor and one reuse step of a first chunk (first launches of every kernel)
+        warm = mk()
+        warm.begin_chunk()
+        wr = warm.rows()
+        for anchor in (True, False):
+            warm.step(Qa[:, :, wr], Ka[:, :, wr], Va[:, :, wr], anchor)
+        torch.cuda.synchronize()
+        del warm
+        st = mk()
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        rec = []
+        for c in range(n_chunks):
+            st.begin_chunk()
+            r = st.rows()
+            Q, K, V = Qa[:, :, r].clone(), Ka[:, :, r].clone(), Va[:, :, r].clone()
+            for s in range(steps):
+                if s:
+                    for X in (Q, K, V):
+                        X += (full.drift * torch.randn(X.shape, generator=gen, device=dev)).to(X.dtype)
+                anchor = s % A == 0
+                scratch.fill_(s & 255)
+                a, b = ev(), ev()
+                a.record(stream)
+                st.step(Q, K, V, anchor, stream=stream)
+                b.record(stream)
+                rec.append((c, anchor, a, b))
+        torch.cuda.synchronize()
+        per = {}
+        for c, anchor, a, b in rec:
+            per.setdefault(c, {"anchor_ms": [], "reuse_ms": []})["anchor_ms" if anchor else "reuse_ms"].append(
+                a.elapsed_time(b))
+        total = sum(a.elapsed_time(b) for _, _, a, b in rec)
+        return per, total, st.chunk_tokens, st.capacity
+
+    res = {m: run(m) for m in ("auto", "two_pass", "single_pass")}
+    per, total, chunk_tokens, capacity = res["auto"]
+    chunks = []
+    for c, v in sorted(per.items()):
+        chunks.append({"chunk": c, "visible_keys": (c + 1) * chunk_tokens,
+                       "anchor_ms": round(statistics.fmean(v["anchor_ms"]), 4),
+                       "anchor_ms_two_pass": round(statistics.fmean(res["two_pass"][0][c]["anchor_ms"]), 4),
+                       "anchor_ms_single_pass": round(statistics.fmean(res["single_pass"][0][c]["anchor_ms"]), 4),
+                       "reuse_ms": round(statistics.fmean(v["reuse_ms"]), 4)})
     out = {"metric": "chunked-causal streaming: ms per chunk (group + anchor + reuse steps)",
            "value": round(total / n_chunks, 4), "unit": "ms", "higher_is_better": False, "n_gpus": 1,
            "dtype": full.dtype, "data": "synthetic",
            "config": {"workload": f"frame-causal video {T}x{Hg}x{Wg} = {T * ft} tokens, B={full.B}, H={full.H}, "
-                                  f"d={full.d}, chunks of {fpc} frames ({st.chunk_tokens} queries), K/V cache "
-                                  f"of {st.capacity} rows, groups of {full.group_size}, k={full.k}, {steps} steps "
-                                  f"per chunk, anchor every {A}",
+                                  f"d={full.d}, chunks of {fpc} frames ({chunk_tokens} queries), K/V cache "
+                                  f"of {capacity} rows, groups of {full.group_size}, k={full.k}, {steps} steps "
+                                  f"per chunk, anchor every {A}, residual R in float32",
                       "chunks": n_chunks, "steps_per_chunk": steps},
-           "chunks": chunks, "cache": "flushed (512 MB overwrite before every timed call)",
+           "value_two_pass": round(res["two_pass"][1] / n_chunks, 4),
+           "value_single_pass": round(res["single_pass"][1] / n_chunks, 4),
+           "chunks": chunks, "anchor_ms_is": "mcs_group + mcs_anchor on the chunk's anchor step",
+           "cache": "flushed (512 MB overwrite before every timed call)",
            "device": torch.cuda.get_device_name(0)}
     print(json.dumps(out), flush=True)
 
@@ -616,6 +632,31 @@ def main():
         torch.cuda.synchronize()
         r16_ms = [a.elapsed_time(b) for a, b in r16_ev]
         del st16
+
+    # the single-pass anchor (group masses on chip, selection in the same
+    # workgroup) on the anchor step, same cold protocol, when the workload's rows fit
+    sp_ms = []
+    try:
+        p1 = mcs.problem_for(w, anchor_mode="single_pass")
+        mcs.workspace_size(p1, mcs.MCS_WS_ANCHOR)
+    except mcs.MCSError:
+        p1 = None
+    if p1 is not None:
+        st1 = mcs.MCSparseAttention(p1)
+        mcs.group(p1, step_in[0][0], st1.perm, st1.ws_group, stream=stream)
+        mcs.anchor(p1, *step_in[0], st1.perm, st1.O, st1.idx, st1.R, st1.ws_anchor, stream=stream)
+        torch.cuda.synchronize()
+        sp_ev = []
+        for i in range(max(1, args.steps // 2)):
+            a, b = ev(), ev()
+            flush()
+            a.record(stream)
+            mcs.anchor(p1, *step_in[0], st1.perm, st1.O, st1.idx, st1.R, st1.ws_anchor, stream=stream)
+            b.record(stream)
+            sp_ev.append((a, b))
+        torch.cuda.synchronize()
+        sp_ms = [a.elapsed_time(b) for a, b in sp_ev]
+        del st1
 
     # block-sparse comparator at the same token budget: mean-pooled block
     # selection from the step's own Q/K, then the gathered attention (no residual)
@@ -797,6 +838,7 @@ def main():
         "dense_frac_at_measured_clock": round(dense_tflops / peak_clk, 4) if peak_clk else None,
         "group_ms": round(statistics.fmean(group_ms), 4),
         "anchor_ms": round(statistics.fmean(anchor_ms), 4),
+        "anchor_ms_single_pass": round(statistics.fmean(sp_ms), 4) if sp_ms else None,
         "period_effective_tflops_dense_equiv": round(A * f_dense / (wall / args.steps) / 1e12, 2),
         # the reuse kernel against the bf16 MFMA peak on the FLOPs it executes; its HBM rate is from
         # counter-measured bytes (traffic), and the rate of its logical gathers (most served by L2 and

@@ -54,6 +54,14 @@ typedef enum mcs_status {
 
 typedef enum mcs_dtype { MCS_F32 = 0, MCS_BF16 = 1 } mcs_dtype;
 
+/* How mcs_anchor forms the selections; both give the same idx bit for bit. */
+typedef enum mcs_anchor_mode {
+  MCS_ANCHOR_AUTO = 0,        /* the library chooses (default)                           */
+  MCS_ANCHOR_TWO_PASS = 1,    /* column-mass matrix in the workspace, then a top-k pass   */
+  MCS_ANCHOR_SINGLE_PASS = 2  /* each group's mass kept on chip and selected in the same  */
+                              /* workgroup; bf16 only, visible keys of the chunk <= 32768 */
+} mcs_anchor_mode;
+
 typedef enum mcs_workspace_kind {
   MCS_WS_GROUP = 0,
   MCS_WS_ANCHOR = 1,
@@ -83,6 +91,7 @@ typedef struct mcs_problem {
                         /* the difference of the float32 outputs stored whole; */
                         /* MCS_BF16 (bf16 problems only) rounds it once more   */
                         /* and halves its bytes                                */
+  int32_t anchor_mode;  /* mcs_anchor_mode (0: automatic)                      */
 } mcs_problem;
 
 /* Bytes of workspace mcs_group (kind MCS_WS_GROUP), mcs_anchor
@@ -127,7 +136,9 @@ mcs_status mcs_dense_attn(const mcs_problem* p, const void* Q, const void* K, co
  * (from mcs_group on this step's Q), it runs exact attention, computes for
  * each group g the exact attention mass every key receives,
  *   m_g[j] = sum_{i in g} exp(scale*<q_i,k_j> - lse_i)   (0 if not visible),
- * keeps the k keys with the largest mass (ties to the lower index), runs
+ * keeps the k keys with the largest mass (ties to the lower index; with
+ * anchor_mode MCS_ANCHOR_SINGLE_PASS each group's masses stay on chip and are
+ * selected in the same pass, see mcs_anchor_mode), runs
  * attention restricted to those keys (softmax renormalised over the selected
  * keys visible to each query; a query with none gets 0) and stores the
  * residual R = O_full - O_sparse.

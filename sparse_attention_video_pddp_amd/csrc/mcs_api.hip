@@ -38,9 +38,19 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Checked {
   mcs::Shape s;
   bool bf16;
-  bool r_f32;  // the residual is float32
+  bool r_f32;        // the residual is float32
+  bool single_pass;  // mcs_anchor keeps each group's mass on chip (mcs_anchor_mode)
   bool empty;
 };
+
+// The automatic anchor mode takes the single pass for rows of visible keys up
+// to this length.  Measured on the frame-causal video (4680 queries, 12
+// heads, d = 128, group + anchor per chunk): 4680 visible keys 1.17 ms single
+// against 1.36 ms two-pass, 9360 keys 1.47 against 1.51, 14040 keys 1.76
+// against 1.68, 32760 keys 3.11 against 2.52; the single pass re-reads the
+// visible K rows for every group, the two-pass path writes and re-reads the
+// mass matrix and launches twice.
+constexpr int kSinglePassAutoKv = 12288;
 
 // Pure host checks of the problem description.
 mcs_status check_problem(const mcs_problem* p, Checked& out) {
@@ -68,6 +78,8 @@ mcs_status check_problem(const mcs_problem* p, Checked& out) {
   if (p->r_dtype != MCS_F32 && p->r_dtype != MCS_BF16) return fail(MCS_ERR_UNSUPPORTED, "r_dtype=%d", p->r_dtype);
   if (p->r_dtype == MCS_BF16 && p->dtype != MCS_BF16)
     return fail(MCS_ERR_UNSUPPORTED, "a bf16 residual needs bf16 inputs (dtype=%d)", p->dtype);
+  if (p->anchor_mode < MCS_ANCHOR_AUTO || p->anchor_mode > MCS_ANCHOR_SINGLE_PASS)
+    return fail(MCS_ERR_INVALID_ARG, "anchor_mode=%d", p->anchor_mode);
   // K and V rows of one head are addressed with 32-bit byte offsets (buffer loads)
   if ((long long)p->Nkv * p->d * 4 > 0x7fffffffLL)
     return fail(MCS_ERR_UNSUPPORTED, "Nkv=%d: one head's K or V exceeds 2^31 bytes", p->Nkv);
@@ -77,6 +89,16 @@ mcs_status check_problem(const mcs_problem* p, Checked& out) {
   out.bf16 = p->dtype == MCS_BF16;
   out.r_f32 = p->r_dtype == MCS_F32;
   out.empty = bh == 0 || p->Nq == 0;
+  out.single_pass = false;
+  if (!out.empty) {
+    const int row = mcs::fused_anchor_row(out.s);
+    const bool fits = out.bf16 && row <= mcs::kFusedMaxKv;
+    if (p->anchor_mode == MCS_ANCHOR_SINGLE_PASS && !fits)
+      return fail(MCS_ERR_UNSUPPORTED, "single-pass anchor needs bf16 inputs and at most %d visible keys (%d)",
+                  mcs::kFusedMaxKv, row);
+    out.single_pass = p->anchor_mode == MCS_ANCHOR_SINGLE_PASS ||
+                      (p->anchor_mode == MCS_ANCHOR_AUTO && fits && row <= kSinglePassAutoKv);
+  }
   return MCS_OK;
 }
 
@@ -123,6 +145,8 @@ size_t anchor_ofull_bytes(const mcs::Shape& s, bool bf16) {
   return bf16 ? round_up((size_t)s.BH * s.Nq * s.d * 4) : 0;
 }
 size_t anchor_mass_bytes_per_head(const mcs::Shape& s) { return round_up((size_t)s.c * s.Nkv * 4); }
+// mass matrix bytes of the anchor: none for the single pass
+size_t anchor_mass_bytes(const Checked& c) { return c.single_pass ? 0 : anchor_mass_bytes_per_head(c.s); }
 
 mcs_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MCS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -187,8 +211,8 @@ mcs_status mcs_workspace_size(const mcs_problem* p, int32_t kind, size_t* bytes,
   } else if (kind == MCS_WS_ANCHOR) {
     if (!c.empty) {
       const size_t fixed = anchor_lse_bytes(c.s) + anchor_ofull_bytes(c.s, c.bf16);
-      need = fixed + (size_t)c.s.BH * anchor_mass_bytes_per_head(c.s);
-      need_min = fixed + anchor_mass_bytes_per_head(c.s);
+      need = fixed + (size_t)c.s.BH * anchor_mass_bytes(c);
+      need_min = fixed + anchor_mass_bytes(c);
     }
   } else if (kind == MCS_WS_BLOCK) {
     need = need_min = c.empty ? 0 : mcs::block_workspace_bytes(c.s);
@@ -240,10 +264,10 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
   if (O == Q || O == K || O == V || R == O || R == Q || R == K || R == V)
     return fail(MCS_ERR_INVALID_ARG, "an output aliases another argument");
   const size_t lse_b = anchor_lse_bytes(c.s), of_b = anchor_ofull_bytes(c.s, c.bf16);
-  const size_t head_b = anchor_mass_bytes_per_head(c.s);
+  const size_t head_b = anchor_mass_bytes(c);
   if (ws_bytes < lse_b + of_b + head_b)
     return fail(MCS_ERR_WORKSPACE, "anchor workspace %zu < minimum %zu bytes", ws_bytes, lse_b + of_b + head_b);
-  const size_t fit = (ws_bytes - lse_b - of_b) / head_b;
+  const size_t fit = head_b ? (ws_bytes - lse_b - of_b) / head_b : (size_t)c.s.BH;
   const int chunk = fit >= (size_t)c.s.BH ? c.s.BH : (int)fit;
   float* lse = (float*)ws;
   // bf16: O_full (float32) in the workspace; float32: straight into R
@@ -253,7 +277,11 @@ mcs_status mcs_anchor(const mcs_problem* p, const void* Q, const void* K, const 
   hipError_t e = c.bf16 ? mcs::launch_dense_bf16(c.s, Q, K, V, O, lse, ofull, st)
                         : mcs::launch_dense_f32(c.s, Q, K, V, O, lse, ofull, st);
   if (e != hipSuccess) return hip_status(e, "mcs_anchor (dense)");
-  for (int bh0 = 0; bh0 < c.s.BH; bh0 += chunk) {
+  if (c.single_pass) {
+    e = mcs::launch_anchor_fused_bf16(c.s, Q, K, perm, lse, idx, st);
+    if (e != hipSuccess) return hip_status(e, "mcs_anchor (single-pass selection)");
+  }
+  for (int bh0 = 0; !c.single_pass && bh0 < c.s.BH; bh0 += chunk) {
     const int nbh = c.s.BH - bh0 < chunk ? c.s.BH - bh0 : chunk;
     e = c.bf16 ? mcs::launch_mass_bf16(c.s, bh0, nbh, Q, K, perm, lse, mass, st)
                : mcs::launch_mass_f32(c.s, bh0, nbh, Q, K, perm, lse, mass, st);

@@ -28,6 +28,15 @@ hipError_t launch_mass_bf16(const Shape& s, int bh0, int nbh, const void* Q, con
 hipError_t launch_mass_f32(const Shape& s, int bh0, int nbh, const void* Q, const void* K,
                            const int32_t* perm, const float* lse, float* mass, hipStream_t st);
 
+// Single-pass anchor selection (bf16): per group, the column mass over the
+// launch's visible keys [0, fused_anchor_row(s)) kept in LDS and its top-k
+// selected in the same workgroup; idx equals the two-pass path's.  Rows of
+// at most kFusedMaxKv keys.
+constexpr int kFusedMaxKv = 32768;
+int fused_anchor_row(const Shape& s);
+hipError_t launch_anchor_fused_bf16(const Shape& s, const void* Q, const void* K, const int32_t* perm,
+                                    const float* lse, int32_t* idx, hipStream_t st);
+
 // Top-k per group row of `mass` (heads [bh0, bh0+nbh)), written to idx[bh][g][k] ascending.
 hipError_t launch_topk(const Shape& s, int bh0, int nbh, const float* mass, int32_t* idx, hipStream_t st);
 

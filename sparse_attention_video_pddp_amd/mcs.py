@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libmcs.so")
 MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
 MCS_F32, MCS_BF16 = 0, 1
 MCS_WS_GROUP, MCS_WS_ANCHOR, MCS_WS_BLOCK, MCS_WS_DRIFT = 0, 1, 2, 3
+MCS_ANCHOR_AUTO, MCS_ANCHOR_TWO_PASS, MCS_ANCHOR_SINGLE_PASS = 0, 1, 2
+_ANCHOR_MODES = {"auto": MCS_ANCHOR_AUTO, "two_pass": MCS_ANCHOR_TWO_PASS, "single_pass": MCS_ANCHOR_SINGLE_PASS}
 MAX_DRIFT_ROWS = 128
 
 EXPORTED = ("mcs_workspace_size", "mcs_group", "mcs_dense_attn", "mcs_anchor", "mcs_sparse_attn",
@@ -31,7 +33,7 @@ class Problem(ctypes.Structure):
                 ("Nkv", ctypes.c_int32), ("d", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("scale", ctypes.c_float), ("causal_block", ctypes.c_int32),
                 ("q_offset", ctypes.c_int32), ("pddp_iters", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("r_dtype", ctypes.c_int32)]
+                ("r_dtype", ctypes.c_int32), ("anchor_mode", ctypes.c_int32)]
 
     def __repr__(self) -> str:
         return "Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -96,17 +98,17 @@ _DTYPES = {"f32": MCS_F32, "bf16": MCS_BF16}
 
 def problem(B: int, H: int, Nq: int, Nkv: int, d: int, group_size: int, k: int, scale: Optional[float] = None,
             causal_block: int = 0, q_offset: int = 0, pddp_iters: int = 32, dtype: str = "bf16",
-            r_dtype: str = "f32") -> Problem:
+            r_dtype: str = "f32", anchor_mode: str = "auto") -> Problem:
     """Problem description; the residual R is float32 unless r_dtype="bf16"
-    (bf16 problems only)."""
+    (bf16 problems only); anchor_mode "auto", "two_pass" or "single_pass"."""
     return Problem(B, H, Nq, Nkv, d, group_size, k, 1.0 / math.sqrt(d) if scale is None else scale,
-                   causal_block, q_offset, pddp_iters, _DTYPES[dtype], _DTYPES[r_dtype])
+                   causal_block, q_offset, pddp_iters, _DTYPES[dtype], _DTYPES[r_dtype], _ANCHOR_MODES[anchor_mode])
 
 
-def problem_for(w, r_dtype: str = "f32") -> Problem:
+def problem_for(w, r_dtype: str = "f32", anchor_mode: str = "auto") -> Problem:
     """Problem of a synthetic workload (``synth.Workload``)."""
     return problem(w.B, w.H, w.Nq, w.Nkv, w.d, w.group_size, w.k, w.scale, w.causal_block, w.q_offset,
-                   w.pddp_iters, w.dtype, r_dtype)
+                   w.pddp_iters, w.dtype, r_dtype, anchor_mode)
 
 
 def _ptr(x) -> Optional[int]:
@@ -319,7 +321,7 @@ class ChunkedCausalStream:
 
     def __init__(self, B: int, H: int, d: int, frame_tokens: int, frames_per_chunk: int, n_chunks: int,
                  group_size: int, k: int, scale: Optional[float] = None, dtype: str = "bf16",
-                 pddp_iters: int = 32, device="cuda"):
+                 pddp_iters: int = 32, device="cuda", r_dtype: str = "f32", anchor_mode: str = "auto"):
         import torch
         self.B, self.H, self.d = B, H, d
         self.frame_tokens = frame_tokens
@@ -327,6 +329,7 @@ class ChunkedCausalStream:
         self.n_chunks = n_chunks
         self.capacity = self.chunk_tokens * n_chunks
         self.G, self.k, self.scale, self.dtype, self.iters = group_size, k, scale, dtype, pddp_iters
+        self.r_dtype, self.anchor_mode = r_dtype, anchor_mode
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.K = torch.zeros((B, H, self.capacity, d), dtype=dt, device=device)
         self.V = torch.zeros_like(self.K)
@@ -337,7 +340,7 @@ class ChunkedCausalStream:
     def problem(self, c: int) -> Problem:
         return problem(self.B, self.H, self.chunk_tokens, self.capacity, self.d, self.G, self.k, self.scale,
                        causal_block=self.frame_tokens, q_offset=c * self.chunk_tokens, pddp_iters=self.iters,
-                       dtype=self.dtype)
+                       dtype=self.dtype, r_dtype=self.r_dtype, anchor_mode=self.anchor_mode)
 
     def rows(self, c: Optional[int] = None) -> slice:
         c = self.chunk if c is None else c

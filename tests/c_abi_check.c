@@ -23,7 +23,8 @@ int main(void) {
   p.B = 1; p.H = 12; p.Nq = 32760; p.Nkv = 32760; p.d = 128; p.group_size = 64; p.k = 1638;
   p.scale = 0.08838834764831845f; p.pddp_iters = 32; p.dtype = MCS_BF16;
   CHECK(p.r_dtype == MCS_F32); /* zero-initialised: float32 residual */
-  CHECK(sizeof(mcs_problem) == 13 * sizeof(int32_t));
+  CHECK(sizeof(mcs_problem) == 14 * sizeof(int32_t));
+  CHECK(p.anchor_mode == MCS_ANCHOR_AUTO);
 
   CHECK(mcs_version() > 0);
   CHECK(strcmp(mcs_status_string(MCS_OK), "MCS_OK") == 0);

@@ -25,12 +25,13 @@ def log(msg: str) -> None:
 
 
 def run_anchor_reuse(w: synth.Workload, heads: Sequence[Tuple[int, int]], anchor_step: int = 0,
-                     reuse_step: int = 1, r_dtype: str = "f32") -> Dict[Tuple[int, int], HeadCase]:
+                     reuse_step: int = 1, r_dtype: str = "f32", anchor_mode: str = "auto"
+                     ) -> Dict[Tuple[int, int], HeadCase]:
     """mcs_group + mcs_anchor on the anchor step's inputs, then mcs_sparse_attn
-    on the reuse step's inputs (residual stored in r_dtype); returns HeadCase
-    per sampled (b, h)."""
+    on the reuse step's inputs (residual stored in r_dtype, selections made
+    in anchor_mode); returns HeadCase per sampled (b, h)."""
     import torch
-    p = mcs.problem_for(w, r_dtype)
+    p = mcs.problem_for(w, r_dtype, anchor_mode)
     log(f"[gpu] {w.name}: {p}")
     (Q0, K0, V0), h0 = device_inputs(w, anchor_step, keep_heads=heads)
     state = mcs.MCSparseAttention(p)

@@ -79,6 +79,31 @@ def test_bad_dtype_rejected():
     assert e.value.status == mcs.MCS_ERR_UNSUPPORTED and "r_dtype" in str(e.value)
 
 
+def test_anchor_mode_field():
+    """anchor_mode: 0 (automatic) by default; an unknown value is refused;
+    the single pass needs bf16 inputs and at most 32768 visible keys; it needs
+    no mass matrix, so its anchor workspace is smaller."""
+    assert base().anchor_mode == mcs.MCS_ANCHOR_AUTO == 0
+    p = base()
+    p.anchor_mode = 3
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.workspace_size(p, mcs.MCS_WS_ANCHOR)
+    assert e.value.status == mcs.MCS_ERR_INVALID_ARG and "anchor_mode" in str(e.value)
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.workspace_size(base(dtype="f32", anchor_mode="single_pass"), mcs.MCS_WS_ANCHOR)
+    assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
+    with pytest.raises(mcs.MCSError) as e:
+        mcs.workspace_size(base(Nkv=40000, k=60, anchor_mode="single_pass"), mcs.MCS_WS_ANCHOR)
+    assert e.value.status == mcs.MCS_ERR_UNSUPPORTED
+    two = mcs.workspace_size(base(anchor_mode="two_pass"), mcs.MCS_WS_ANCHOR)
+    one = mcs.workspace_size(base(anchor_mode="single_pass"), mcs.MCS_WS_ANCHOR)
+    c = -(-1000 // 64)
+    assert one[0] == one[1] and two[1] - one[1] >= 4 * c * 1200 and two[0] - one[0] >= 2 * 4 * c * 1200
+    # a causal query chunk whose queries see only the first 2 of 10 frames of a long cache
+    causal = base(Nq=256, Nkv=64 * 1024, k=600, causal_block=1024, q_offset=1024, anchor_mode="single_pass")
+    mcs.workspace_size(causal, mcs.MCS_WS_ANCHOR)
+
+
 def test_residual_dtype_defaults_to_float32():
     """A problem with r_dtype left at zero keeps R in float32; every kept-key
     count up to Nkv is accepted (no on-chip table limits k)."""
@@ -87,7 +112,7 @@ def test_residual_dtype_defaults_to_float32():
     assert base(r_dtype="bf16").r_dtype == mcs.MCS_BF16
     for k in (1, 28673, 40000):
         mcs.workspace_size(base(Nkv=40000, k=k), mcs.MCS_WS_ANCHOR)
-    assert ctypes.sizeof(mcs.Problem) == 13 * 4
+    assert ctypes.sizeof(mcs.Problem) == 14 * 4
 
 
 def test_null_and_misaligned_pointers_rejected():
@@ -116,7 +141,7 @@ def test_empty_problem_is_a_noop_without_pointers():
 
 
 def test_workspace_sizes():
-    p = base()
+    p = base(anchor_mode="two_pass")
     g, gmin = mcs.workspace_size(p, mcs.MCS_WS_GROUP)
     assert g == gmin and g >= 2 * 4 * 2 * 1000
     a, amin = mcs.workspace_size(p, mcs.MCS_WS_ANCHOR)
@@ -124,7 +149,7 @@ def test_workspace_sizes():
     assert amin >= 4 * 2 * 1000 + 4 * c * 1200
     assert a >= amin + 4 * c * 1200
     # bf16: the anchor also keeps the float32 dense output of every head (2 heads x 1000 x 128)
-    a32, amin32 = mcs.workspace_size(base(dtype="f32"), mcs.MCS_WS_ANCHOR)
+    a32, amin32 = mcs.workspace_size(base(dtype="f32", anchor_mode="two_pass"), mcs.MCS_WS_ANCHOR)
     assert amin - amin32 >= 4 * 2 * 1000 * 128 and a - a32 == amin - amin32
     with pytest.raises(mcs.MCSError) as e:
         mcs.workspace_size(p, 9)

@@ -265,3 +265,56 @@ def test_side_stream_gives_the_default_stream_results(cuda):
     side = run(torch.cuda.Stream())
     for a, b in zip(ref, side):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["bidir_small", "causal_small", "causal_mid", "large_small", "stress_small",
+                                  "d64_g64", "offset_d128_g64", "batch_small"])
+def test_single_pass_anchor_equals_two_pass(cuda, name):
+    """The single-pass anchor (each group's column mass kept on chip and
+    selected in the same workgroup) computes every mass with the two-pass
+    path's arithmetic: the selections, and therefore the residual and the
+    anchor and reuse outputs, are equal bit for bit; the single pass is also
+    checked against the oracle stage by stage."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    from tests.gpu_runner import log, run_anchor_reuse
+    w = SMALL[name]
+    (Q0, K0, V0), _ = device_inputs(w, 0)
+    (Q1, K1, V1), _ = device_inputs(w, 1)
+    res = {}
+    for mode in ("two_pass", "single_pass"):
+        st = mcs.MCSparseAttention(mcs.problem_for(w, anchor_mode=mode))
+        Oa = st.step(Q0, K0, V0, True).clone()
+        Or = st.step(Q1, K1, V1, False).clone()
+        torch.cuda.synchronize()
+        res[mode] = (st.perm.clone(), st.idx.clone(), st.R.clone(), Oa, Or)
+    for a, b in zip(res["two_pass"], res["single_pass"]):
+        assert torch.equal(a, b)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    cases = run_anchor_reuse(w, heads, anchor_mode="single_pass")
+    for bh, case in cases.items():
+        reps = check_head(case, w.group_size, w.k, w.scale, w.causal_block, w.q_offset, w.pddp_iters)
+        for r in reps:
+            log(f"  {name} (single pass) head {bh}: {r}")
+        assert_reports(reps, f"{name} (single pass) head {bh}")
+
+
+@pytest.mark.parametrize("chunk", [0, 3, 6])
+def test_single_pass_anchor_at_full_size(cuda, chunk):
+    """Chunks of the frame-causal video at full size (4680 queries over a
+    32760-row K/V cache, 12 heads; chunk c sees 4680 (c + 1) keys, up to the
+    single pass's largest row): both anchor modes give the same selections."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    base = synth.get("causal")
+    w = base.with_(name=f"causal_chunk{chunk}", q_frames=(3 * chunk, 3 * chunk + 3))
+    (Q, K, V), _ = device_inputs(w, 0)
+    idx = {}
+    for mode in ("two_pass", "single_pass"):
+        st = mcs.MCSparseAttention(mcs.problem_for(w, anchor_mode=mode))
+        st.step(Q, K, V, True)
+        torch.cuda.synchronize()
+        idx[mode] = st.idx.clone()
+    assert torch.equal(idx["two_pass"], idx["single_pass"])
