@@ -82,6 +82,36 @@ __device__ __forceinline__ void split_shifted(bf16x8 x, float r, bf16x8& hi, bf1
   }
 }
 
+// The rows of an LDS tile (ring.hpp layout: row-major, 16-byte chunks
+// XOR-swizzled per row) shifted by r and split in place: each chunk x of 8
+// channels becomes hi = bf16(x - r), and the chunk at the same offset of `lo`
+// becomes bf16(x - r - hi) (split_shifted).  Each element is split once, by
+// one thread; the MFMA operands are then read from both tiles as they are.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void split_tile(unsigned char* slot, unsigned char* lo, const float* sRf) {
+  constexpr int CH = D / 8;
+  static_assert((ROWS * CH) % NT == 0, "chunks per thread");
+#pragma unroll 1
+  for (int k = 0; k < ROWS * CH / NT; ++k) {
+    const int ci = k * NT + (int)threadIdx.x;
+    const int row = ci / CH, pos = ci % CH;
+    const int ch = 8 * (pos ^ swz<D>(row));  // first channel of the chunk
+    bf16x8* px = (bf16x8*)(slot + row * (2 * D) + 16 * pos);
+    const bf16x8 x = *px;
+    const f32x4 ra = *(const f32x4*)(sRf + ch), rb = *(const f32x4*)(sRf + ch + 4);
+    bf16x8 h, l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float y = (float)x[j] - (j < 4 ? ra[j] : rb[j - 4]);
+      const __bf16 hj = (__bf16)y;
+      h[j] = hj;
+      l[j] = (__bf16)(y - (float)hj);
+    }
+    *px = h;
+    *(bf16x8*)(lo + row * (2 * D) + 16 * pos) = l;
+  }
+}
+
 // Shape of node `slot` of `level` (c == 0: the slot lies under a leaf).
 __device__ __forceinline__ Node pddp_node(int slot, int level, int Nq, int G) {
   Node nd{0, Nq, (Nq + G - 1) / G};
@@ -114,6 +144,7 @@ template <int D, bool BF16>
 struct GramLds {
   static constexpr int SLOT0 = BF16 ? GramCfg<D>::TILE_BYTES : 64 * GramCfg<D>::FS * 4;
   static constexpr int SLOT1 = BF16 ? GramCfg<D>::TILE_BYTES : 16;
+  static constexpr int SLOTLO = BF16 ? GramCfg<D>::TILE_BYTES : 16;  // low parts of the split tile
 };
 
 // Step 1 over member rows [r0, r1) of a node (nperm: the node's members).
@@ -123,7 +154,8 @@ struct GramLds {
 // Ends with a barrier.
 template <int D, bool BF16>
 __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
-                          unsigned char* slot0, unsigned char* slot1, double (&cacc)[D / 32][16], double* sS) {
+                          unsigned char* slot0, unsigned char* slot1, unsigned char* slotlo, float* sRf,
+                          double (&cacc)[D / 32][16], double* sS) {
   using C = GramCfg<D>;
   constexpr int NB = C::NB;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
@@ -143,12 +175,9 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     const int ob1 = (8 + vr) * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(8 + vr));
     const int lrow0 = l / C::CH, lchunk = l % C::CH;
     const int ntiles = (r1 - r0 + 63) / 64;
-    // the shift: this lane's channels of the node's first member row
-    const __bf16* rrow = Qh + (size_t)nperm[0] * D;
-    float rv[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) rv[b] = (float)rrow[32 * b + ln];
-    const float rw = (float)rrow[32 * min(w, NB - 1) + ln];
+    // the shift r: the node's first member row, in LDS as float32 (published by
+    // the first barrier of the tile loop)
+    if (tid < D) sRf[tid] = (float)Qh[(size_t)nperm[0] * D + tid];
     // column sums: lane (n, h) of wave w keeps element n%16 of the ones-product,
     // i.e. S[32w + 8((n%16)/4) + 4h + n%4]
     double sacc = 0.0;
@@ -173,16 +202,15 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     bf16x8 ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (__bf16)1.0f;
-    // shifted y^T operand of channel block b (shift r) for 16-row step ks2 as
-    // two bf16 parts (tail rows of the last tile are the shift row: zero)
-    auto operand = [&](const unsigned char* slot, int b, float r, int ks2, bf16x8& hi, bf16x8& lo) {
-      const unsigned char* base = slot + 16 * (2 * D) * ks2;
-      split_shifted(cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b)))), r, hi, lo);
+    // y^T operand of channel block b for 16-row step ks2 from a split tile (hi or lo part)
+    auto operand = [&](const unsigned char* t, int b, int ks2) {
+      const unsigned char* base = t + 16 * (2 * D) * ks2;
+      return cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
     };
-    // one fp32 accumulator live at a time (row blocks outer) and this wave's
-    // own operand re-read for each block, which keeps the kernel within 256
-    // registers per lane (a chain of dependent MFMAs issues as fast as
-    // independent ones); y y^T = (hi + lo)(hi + lo)^T as four exact products
+    // one fp32 accumulator live at a time (row blocks outer), which keeps the
+    // kernel within 256 registers per lane (a chain of dependent MFMAs issues
+    // as fast as independent ones); y y^T = (hi + lo)(hi + lo)^T as four exact
+    // products
     auto compute = [&](const unsigned char* slot) {
       if (w >= NB) return;
       f32x16 accS = {};
@@ -191,9 +219,8 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
         f32x16 acc = {};
 #pragma unroll
         for (int ks2 = 0; ks2 < 4; ++ks2) {
-          bf16x8 wh, wl, hb, lb;
-          operand(slot, w, rw, ks2, wh, wl);
-          operand(slot, bi, rv[bi], ks2, hb, lb);
+          const bf16x8 wh = operand(slot, w, ks2), wl = operand(slotlo, w, ks2);
+          const bf16x8 hb = operand(slot, bi, ks2), lb = operand(slotlo, bi, ks2);
           acc = mfma_32x32x16(hb, wh, acc);
           acc = mfma_32x32x16(hb, wl, acc);
           acc = mfma_32x32x16(lb, wh, acc);
@@ -211,6 +238,9 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
       for (int i = 1; i < 16; ++i) sv = (si == i) ? accS[i] : sv;
       sacc += (double)sv;
     };
+    // tile t lands in its slot (double-buffered copies); after a barrier it is
+    // split in place (the low parts in slotlo, single-buffered: every wave has
+    // finished the previous tile at that barrier), then, after another, used
     if (ntiles > 0) {
       load_ids(0);
       issue(slot0);
@@ -223,6 +253,8 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
         issue(slot1);
         if (t + 2 < ntiles) load_ids(t + 2);
       }
+      split_tile<D, 64, 256>(slot0, slotlo, sRf);
+      __syncthreads();
       compute(slot0);
       if (t + 1 >= ntiles) break;
       wait_vmcnt<0>();
@@ -231,6 +263,8 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
         issue(slot0);
         if (t + 3 < ntiles) load_ids(t + 3);
       }
+      split_tile<D, 64, 256>(slot1, slotlo, sRf);
+      __syncthreads();
       compute(slot1);
     }
     if (w < NB && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = sacc;
@@ -432,9 +466,15 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   using Sel = BlockSelect<kNodeThreads, VPT>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[L::SLOT0];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
+  __shared__ __attribute__((aligned(1024))) unsigned char slotlo[L::SLOTLO];
+  __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D], sR[D], sV[D], sY[2][D], sRed[2][4];
   __shared__ typename Sel::Shared sh;
-  __shared__ uint32_t s_keys[VPT * kNodeThreads];
+  // the projection keys reuse the first tile slot once the scatter sums are
+  // done (when they fit: d = 128)
+  constexpr bool kKeysInSlot = VPT * kNodeThreads * 4 <= L::SLOT0;
+  __shared__ uint32_t s_keys_own[kKeysInSlot ? 1 : VPT * kNodeThreads];
+  uint32_t* const s_keys = kKeysInSlot ? (uint32_t*)slot0 : s_keys_own;
   const int bh = blockIdx.y;
   const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
   if (nd.c <= 1) return;
@@ -442,7 +482,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   int32_t* nperm = p.perm + hbase + nd.start;
   if (BF16 && (int)threadIdx.x < D) sR[threadIdx.x] = (double)(float)((const __bf16*)p.Q)[(hbase + nperm[0]) * D + threadIdx.x];
   double cacc[D / 32][16];
-  gram_rows<D, BF16>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, cacc, sS);  // its final barrier publishes sR
+  gram_rows<D, BF16>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, slotlo, sRf, cacc, sS);  // its final barrier publishes sR
   const double muv = centre_and_iterate<D>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
   project_rows<D, BF16, kNodeThreads>(p.Q, hbase, nperm, 0, nd.n, sV, muv, [&](int i, uint32_t k) { s_keys[i] = k; });
   __syncthreads();
@@ -486,6 +526,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   using Sel = BlockSelect<kNodeThreads, VPT>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char slotlo[TILE];
+  __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D], sR[D], sV[D], sMu[4];
   __shared__ float sY[2][D], sRed[2][4];
   __shared__ typename Sel::Shared sh;
@@ -502,12 +544,11 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
 
   // ---- 1. scatter sums of the shifted rows, fp32 over all tiles ---------------
   const __bf16* Qh = (const __bf16*)p.Q + hbase * D;
-  const __bf16* rrow = Qh + (size_t)nperm[0] * D;  // the shift r
-  if (tid < D) sR[tid] = (double)(float)rrow[tid];
-  float rv[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) rv[b] = (float)rrow[32 * b + ln];
-  const float rw = (float)rrow[32 * min(w, NB - 1) + ln];
+  const __bf16* rrow = Qh + (size_t)nperm[0] * D;  // the shift r (published by the tile loop's first barrier)
+  if (tid < D) {
+    sR[tid] = (double)(float)rrow[tid];
+    sRf[tid] = (float)rrow[tid];
+  }
   const int vr = 4 * h + ((l & 15) >> 2);
   const int c0 = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
   const int ob0 = vr * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(vr));
@@ -535,20 +576,19 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   f32x16 acc[NB], accS = {};
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+  // y^T operands from the split tile (hi part in the slot, lo part in slotlo)
   auto compute = [&](const unsigned char* slot) {
     if (!gw) return;
 #pragma unroll
     for (int ks2 = 0; ks2 < TR / 16; ++ks2) {
-      const unsigned char* base = slot + 16 * (2 * D) * ks2;
-      auto part = [&](int b, float r, bf16x8& hi, bf16x8& lo) {
-        split_shifted(cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b)))), r, hi, lo);
+      auto part = [&](const unsigned char* t, int b) {
+        const unsigned char* base = t + 16 * (2 * D) * ks2;
+        return cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
       };
-      bf16x8 wh, wl;  // this wave's column block
-      part(w, rw, wh, wl);
+      const bf16x8 wh = part(slot, w), wl = part(slotlo, w);  // this wave's column block
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) {
-        bf16x8 hb, lb;
-        part(bi, rv[bi], hb, lb);
+        const bf16x8 hb = part(slot, bi), lb = part(slotlo, bi);
         acc[bi] = mfma_32x32x16(hb, wh, acc[bi]);
         acc[bi] = mfma_32x32x16(hb, wl, acc[bi]);
         acc[bi] = mfma_32x32x16(lb, wh, acc[bi]);
@@ -558,6 +598,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       accS = mfma_32x32x16(wl, ones, accS);
     }
   };
+  // tile t lands in its slot (double-buffered copies); after a barrier it is
+  // split in place (low parts in slotlo, single-buffered: every wave has
+  // finished the previous tile at that barrier), then, after another, used
   load_ids(0);
   issue(slot0);
   if (ntiles > 1) load_ids(1);
@@ -568,6 +611,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       issue(slot1);
       if (t + 2 < ntiles) load_ids(t + 2);
     }
+    split_tile<D, TR, kNodeThreads>(slot0, slotlo, sRf);
+    __syncthreads();
     compute(slot0);
     if (t + 1 >= ntiles) break;
     wait_vmcnt<0>();
@@ -576,6 +621,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       issue(slot0);
       if (t + 3 < ntiles) load_ids(t + 3);
     }
+    split_tile<D, TR, kNodeThreads>(slot1, slotlo, sRf);
+    __syncthreads();
     compute(slot1);
   }
   // column sums: lane (n, h) of wave w keeps element n%16: S[32w + 8((n%16)/4) + 4h + n%4]
@@ -666,6 +713,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   using L = GramLds<D, BF16>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[L::SLOT0];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
+  __shared__ __attribute__((aligned(1024))) unsigned char slotlo[L::SLOTLO];
+  __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D];
   const int bh = blockIdx.y, slot = blockIdx.x / p.pmax, chunk = blockIdx.x % p.pmax;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
@@ -675,7 +724,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int r1 = min(nd.n, r0 + p.cr);
   const size_t hbase = (size_t)bh * p.Nq;
   double cacc[D / 32][16];
-  gram_rows<D, BF16>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, cacc, sS);
+  gram_rows<D, BF16>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, slotlo, sRf, cacc, sS);
   const int nslots = 1 << p.level;
   double* out = p.part + (((size_t)bh * nslots + slot) * p.pmax + chunk) * (D + D * D);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
