@@ -88,15 +88,16 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def load_traffic(kernel: str, config: str):
-    """HBM bytes per launch measured with rocprofv3 counters, if they were
-    taken on the current kernel source; else None."""
+    """HBM bytes per launch of a kernel instantiation (full name, e.g.
+    "sparse_ring_kernel<128, 64, true>") measured with rocprofv3 counters, if
+    they were taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(kernel, {}).get(config)
-    if not e or e.get("source_hash") != kernel_source_hash(kernel):
+    if not e or e.get("source_hash") != kernel_source_hash(kernel.split("<")[0]):
         return None
     return e.get("bytes_per_launch")
 
@@ -115,7 +116,7 @@ def load_clock(kernel: str, config: str):
     except (OSError, ValueError):
         return None
     e = t.get(kernel, {}).get(config)
-    if not e or e.get("source_hash") != kernel_source_hash(kernel):
+    if not e or e.get("source_hash") != kernel_source_hash(kernel.split("<")[0]):
         return None
     return e.get("mhz")
 
@@ -128,8 +129,15 @@ def _short_kernel(name: str) -> str:
         rest = name[m.end():]
         ident, rest = rest[:n], rest[n:]
         pretty = []
-        for a in re.finditer(r"DF16b|Li(\d+)E|(?<=I)f|(?<=E)f", rest.split("EEv")[0]):
-            pretty.append("__bf16" if a.group(0) == "DF16b" else (a.group(1) if a.group(1) else "float"))
+        for a in re.finditer(r"DF16b|Li(\d+)E|Lb([01])E|(?<=I)f|(?<=E)f", rest.split("EEv")[0]):
+            if a.group(0) == "DF16b":
+                pretty.append("__bf16")
+            elif a.group(1):
+                pretty.append(a.group(1))
+            elif a.group(2):
+                pretty.append("true" if a.group(2) == "1" else "false")
+            else:
+                pretty.append("float")
         return ident + (f"<{', '.join(pretty)}>" if pretty else "")
     name = name.replace("void ", "").replace("mcs::(anonymous namespace)::", "")
     return re.sub(r"\(.*$", "", name)
@@ -144,13 +152,14 @@ def launch_label(kernel: str, prev: str) -> str:
     flush, so a launch right after the flush fill is a timed (cold) call and
     keeps the plain kernel name: those rows are comparable with the live
     HIP-event timings.  The gathered-attention kernel otherwise is the anchor's
-    epilogue (after a top-k launch: it forms R), the block-sparse comparator
+    epilogue (after a top-k or single-pass selection launch: it forms R), the
+    block-sparse comparator
     (after a block selection) or an untimed call (warm-cache or fidelity
     pass); the dense kernel after a PDDP launch is the anchor's exact pass,
     else an untimed call."""
     cold = FLUSH_KERNEL in prev
     if kernel.startswith("sparse_ring_kernel"):
-        if prev.startswith("topk_kernel"):
+        if prev.startswith("topk_kernel") or prev.startswith("anchor_fused"):
             return kernel + " (anchor epilogue)"
         if prev.startswith("block_select"):
             return kernel + " (block-sparse comparator)"
@@ -243,7 +252,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, config: str, cmd_fetch: s
                      f"{(fb + wb) / 1e6:.1f} |")
         base = k.split("<")[0]
         if base in KERNEL_SOURCES and "(" not in k:
-            table.setdefault(base, {})[config] = {
+            table.setdefault(k, {})[config] = {
                 "bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                 "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
                 "launches": len(per["FETCH_SIZE"][k]), "source_hash": kernel_source_hash(base)}
@@ -291,7 +300,7 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
     for k, d in vals.items():
         base = k.split("<")[0]
         if "cyc_per_ns" in d and base in KERNEL_SOURCES and "(" not in k:  # timed launches only
-            clock.setdefault(base, {})[config] = {
+            clock.setdefault(k, {})[config] = {
                 "mhz": round(statistics.fmean(d["cyc_per_ns"]) / N_XCD * 1e3, 1),
                 "launches": len(d["cyc_per_ns"]), "source_hash": kernel_source_hash(base)}
     if clock:
@@ -300,8 +309,8 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
                 table = json.load(fh)
         except (OSError, ValueError):
             table = {}
-        for base, e in clock.items():
-            table.setdefault(base, {}).update(e)
+        for k, e in clock.items():
+            table.setdefault(k, {}).update(e)
         with open(CLOCK_FILE, "w") as fh:
             json.dump(table, fh, indent=1, sort_keys=True)
     with open(out, "w") as f:
@@ -648,8 +657,10 @@ def main():
         torch.cuda.synchronize()
         sp_ev = []
         for i in range(max(1, args.steps // 2)):
+            # as in the timed periods: grouping right after the flush, the anchor after it
             a, b = ev(), ev()
             flush()
+            mcs.group(p1, step_in[0][0], st1.perm, st1.ws_group, stream=stream)
             a.record(stream)
             mcs.anchor(p1, *step_in[0], st1.perm, st1.O, st1.idx, st1.R, st1.ws_anchor, stream=stream)
             b.record(stream)
@@ -774,8 +785,11 @@ def main():
     dense_eq = f_dense / (r_mean * 1e-3) / 1e12          # the dense work it stands in for, per second
     dense_tflops = f_dense / (d_mean * 1e-3) / 1e12
     rbytes = reuse_bytes_per_launch(w)
-    traffic = load_traffic("sparse_ring_kernel", w.name)
-    mhz = load_clock("dense_bf16_kernel", w.name)
+    # the instantiations the timed calls launch (bf16: float32 residual; d, G of the workload)
+    sparse_name = f"sparse_ring_kernel<{w.d}, {w.group_size}, true>"
+    dense_name = f"dense_bf16_kernel<{w.d}, 8>"
+    traffic = load_traffic(sparse_name, w.name)
+    mhz = load_clock(dense_name, w.name)
     peak_clk = cus * mhz * 1e6 * 4096 / 1e12 if cus and mhz else None
     out = {
         "metric": METRIC,
@@ -843,7 +857,7 @@ def main():
         # the reuse kernel against the bf16 MFMA peak on the FLOPs it executes; its HBM rate is from
         # counter-measured bytes (traffic), and the rate of its logical gathers (most served by L2 and
         # the Infinity Cache, so above any HBM figure) is reported apart, never as a fraction
-        "roofline": {"kernel": "sparse_ring_kernel (mcs_sparse_attn, reuse step)", "bound": "mfma",
+        "roofline": {"kernel": f"{sparse_name} (mcs_sparse_attn, reuse step)", "bound": "mfma",
                      "achieved": round(exec_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(exec_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
@@ -853,10 +867,10 @@ def main():
                      "traffic_frac": round(traffic / (r_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if traffic else None,
                      "logical_gather_bytes_per_launch": rbytes,
                      "logical_gather_gbs": round(rbytes / (r_mean * 1e-3) / 1e9, 1)},
-        "roofline_dense": {"kernel": "dense_bf16_kernel (mcs_dense_attn)", "bound": "mfma",
+        "roofline_dense": {"kernel": f"{dense_name} (mcs_dense_attn)", "bound": "mfma",
                            "achieved": round(dense_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
-                           "traffic": load_traffic("dense_bf16_kernel", w.name)},
+                           "traffic": load_traffic(dense_name, w.name)},
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

@@ -53,7 +53,8 @@ def test_launch_labels_follow_the_previous_kernel():
 
 
 FILL = "void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<unsigned char>, std::array<char*, 1ul> >(int)"
-SPARSE = "void mcs::(anonymous namespace)::sparse_ring_kernel<128, 64>(mcs::(anonymous namespace)::Params)"
+SPARSE = "void mcs::(anonymous namespace)::sparse_ring_kernel<128, 64, true>(mcs::(anonymous namespace)::Params)"
+SPARSE_SHORT = "sparse_ring_kernel<128, 64, true>"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -85,7 +86,7 @@ def test_traffic_summary_scales_by_the_copy_and_keeps_timed_launches(tmp_path, m
     _counter_csv(tmp_path / "w.csv", write)
     bench.summarize_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cfg", "cmd-f", "cmd-w")
     import json
-    t = json.load(open(tmp_path / "profiles" / "traffic.json"))["sparse_ring_kernel"]["cfg"]
+    t = json.load(open(tmp_path / "profiles" / "traffic.json"))[SPARSE_SHORT]["cfg"]
     assert t["fetch_factor"] == 2.0 and t["write_factor"] == 1.0 and t["launches"] == 1
     assert t["fetch_bytes"] == round(1000.0 * 1024 * 2) and t["write_bytes"] == round(100.0 * 1024)
     assert t["source_hash"] == "hash-sparse_ring_kernel"
@@ -93,7 +94,7 @@ def test_traffic_summary_scales_by_the_copy_and_keeps_timed_launches(tmp_path, m
     assert "cmd-f" in md and "(untimed: warm-cache or fidelity call)" in md
 
 
-def test_counter_summary_writes_the_cycle_columns(tmp_path):
+def test_counter_summary_writes_the_cycle_columns(tmp_path, monkeypatch):
     """GRBM_GUI_ACTIVE per dispatch becomes cycles per launch and cycles per
     ns of the dispatch's own duration; columns of absent counters are left
     out."""
@@ -102,9 +103,14 @@ def test_counter_summary_writes_the_cycle_columns(tmp_path):
     rows = [(FILL, "GRBM_GUI_ACTIVE", 2e3, 100), (SPARSE, "GRBM_GUI_ACTIVE", 8e6, 500000)]
     _counter_csv(tmp_path / "c.csv", rows)
     out = tmp_path / "clock.md"
+    monkeypatch.setattr(bench, "CLOCK_FILE", str(tmp_path / "clock.json"))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "hash-" + k)
     bench.summarize_pmc(str(out), [(str(tmp_path / "c.csv"), "the command")], "T", "N")
+    import json
+    c = json.load(open(tmp_path / "clock.json"))[SPARSE_SHORT]["bidir5"]
+    assert c["mhz"] == 2000.0 and c["source_hash"] == "hash-sparse_ring_kernel"  # 16 cycles/ns over 8 XCDs
     md = open(out).read()
     assert "GRBM_GUI_ACTIVE (M cycles)" in md and "MFMA busy %" not in md
-    row = [l for l in md.splitlines() if l.startswith("| `sparse_ring_kernel<128, 64>`")][0]
+    row = [l for l in md.splitlines() if l.startswith("| `sparse_ring_kernel<128, 64, true>`")][0]
     cells = [c.strip() for c in row.split("|")[1:-1]]
     assert cells[1] == "1" and cells[2] == "500.0" and cells[3] == "8.00" and cells[4] == "16.000"
