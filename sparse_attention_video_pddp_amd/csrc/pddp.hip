@@ -31,9 +31,12 @@
 // ids kept in registers.
 //
 // In step 1 the gathered rows of a 64-row tile are copied straight into LDS
-// (global_load_lds, 16 bytes per lane) in a two-slot ring, row-major with the
-// 16-byte chunks XOR-swizzled per row; both MFMA operands (x^T blocks) are
-// read with ds_read_b64_tr_b16.  Wave w holds column block w of the scatter
+// (global_load_lds, 16 bytes per lane) in a ring of two slots (one workgroup
+// per node) or three (row chunks of the many-workgroup levels, and the
+// small-node kernel's 32-row tiles), row-major with the 16-byte chunks
+// XOR-swizzled per row; both MFMA operands (x^T blocks) are read with
+// ds_read_b64_tr_b16.  The partial sums of the many-workgroup levels cover
+// chunks of cg rows, about 512 chunks over all heads at the top level.  Wave w holds column block w of the scatter
 // matrix in the MFMA output layout (lane: one column, 16 rows per 32-row
 // block), so C v needs only an in-lane sum and one half-wave exchange.
 #include <algorithm>
@@ -61,6 +64,7 @@ struct PddpParams {
   double* red;   // [BH][nslots][D + D*D] their sums
   double* vec;   // [BH][nslots][D + 1] direction v and (S/n) . v
   int Nq, G, iters, level, cr, pmax;
+  int cg;       // rows per partial scatter sum (a chunk of a node) at the many-workgroup levels
   int pj_pmax;  // projection chunks (of kProjRows rows) per node at this level
 };
 
@@ -144,6 +148,7 @@ template <int D, bool BF16>
 struct GramLds {
   static constexpr int SLOT0 = BF16 ? GramCfg<D>::TILE_BYTES : 64 * GramCfg<D>::FS * 4;
   static constexpr int SLOT1 = BF16 ? GramCfg<D>::TILE_BYTES : 16;
+  static constexpr int SLOT2 = BF16 ? GramCfg<D>::TILE_BYTES : 16;
   static constexpr int SLOTLO = BF16 ? GramCfg<D>::TILE_BYTES : 16;  // low parts of the split tile
 };
 
@@ -152,10 +157,10 @@ struct GramLds {
 // 4*h + i%4, column 32*w + lane%32.  sS[0..D): sum y.  For bf16 rows
 // y = x - Q[nperm[0]] (the node's first member row), for fp32 rows y = x.
 // Ends with a barrier.
-template <int D, bool BF16>
+template <int D, bool BF16, int NS>
 __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
-                          unsigned char* slot0, unsigned char* slot1, unsigned char* slotlo, float* sRf,
-                          double (&cacc)[D / 32][16], double* sS) {
+                          unsigned char* slot0, unsigned char* slot1, unsigned char* slot2, unsigned char* slotlo,
+                          float* sRf, double (&cacc)[D / 32][16], double* sS) {
   using C = GramCfg<D>;
   constexpr int NB = C::NB;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
@@ -182,6 +187,7 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     // i.e. S[32w + 8((n%16)/4) + 4h + n%4]
     double sacc = 0.0;
     const int si = ln & 15;
+    // member ids of the tile to be copied next (loaded a tile before its copy is issued)
     int ids[C::LPW];
     auto load_ids = [&](int t) {
 #pragma unroll
@@ -238,34 +244,37 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
       for (int i = 1; i < 16; ++i) sv = (si == i) ? accS[i] : sv;
       sacc += (double)sv;
     };
-    // tile t lands in its slot (double-buffered copies); after a barrier it is
-    // split in place (the low parts in slotlo, single-buffered: every wave has
-    // finished the previous tile at that barrier), then, after another, used
-    if (ntiles > 0) {
-      load_ids(0);
-      issue(slot0);
-      if (ntiles > 1) load_ids(1);
+    static_assert(NS == 2 || NS == 3, "ring depth");
+    unsigned char* const ring[3] = {slot0, slot1, slot2};
+    // Tile t lands in ring slot t % NS by direct-to-LDS copies issued NS-1
+    // tiles ahead; after a barrier it is split in place (the low parts in
+    // slotlo, single-buffered: every wave has finished the previous tile at
+    // that barrier), then, after another, used.  Per tile a wave issues LPW
+    // copies and then LPW id loads, so when tile t is waited for, the loads
+    // issued after its copies are ids(t+1) and, per later tile in flight, its
+    // copies and the next ids: (2 NS - 3) LPW in all.
+    for (int k = 0; k < NS - 1 && k < ntiles; ++k) {
+      load_ids(k);
+      issue(ring[k]);
     }
-    for (int t = 0; t < ntiles; t += 2) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (t + 1 < ntiles) {
-        issue(slot1);
-        if (t + 2 < ntiles) load_ids(t + 2);
+    if (NS - 1 < ntiles) load_ids(NS - 1);
+    // unrolled by NS so that every slot address is a constant of its copy
+    for (int t0 = 0; t0 < ntiles; t0 += NS) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int t = t0 + k;
+        if (t >= ntiles) break;
+        if (t + NS - 1 < ntiles) wait_vmcnt<(2 * NS - 3) * C::LPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (t + NS - 1 < ntiles) {
+          issue(ring[(k + NS - 1) % NS]);  // the slot of tile t-1, whose last reads ended before the barrier
+          if (t + NS < ntiles) load_ids(t + NS);
+        }
+        split_tile<D, 64, 256>(ring[k], slotlo, sRf);
+        __syncthreads();
+        compute(ring[k]);
       }
-      split_tile<D, 64, 256>(slot0, slotlo, sRf);
-      __syncthreads();
-      compute(slot0);
-      if (t + 1 >= ntiles) break;
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (t + 2 < ntiles) {
-        issue(slot0);
-        if (t + 3 < ntiles) load_ids(t + 3);
-      }
-      split_tile<D, 64, 256>(slot1, slotlo, sRf);
-      __syncthreads();
-      compute(slot1);
     }
     if (w < NB && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = sacc;
     __syncthreads();
@@ -308,7 +317,7 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
 // With v_k = y_k / ||y_k||, the iteration runs as y_{k+1} = C y_k / ||y_k||:
 // the norm of y_k is reduced while y_{k+1} is formed, so one barrier per step
 // suffices (y double-buffered in sY).  If C v_k = 0 the direction stays v_k.
-template <int D>
+template <int D, int YB>
 __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* sS, const double* sR, double* sV,
                                      double (*sY)[D], double (*sRed)[4], int n, int iters) {
   constexpr int NB = D / 32;
@@ -329,6 +338,17 @@ __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* s
   int cur = 0;   // buffer holding y_k
   int last = 0;  // buffer of the last y with a nonzero norm
   for (int it = 0; it < iters; ++it) {
+    // this lane's rows of y_k, read YB row blocks at a time before they are
+    // used (the reads' latencies overlap; YB < NB bounds the registers)
+    static_assert(NB % YB == 0, "row blocks per read batch");
+    double2 yv[YB][8];
+    auto read_y = [&](int b0) {
+#pragma unroll
+      for (int j = 0; j < YB; ++j)
+#pragma unroll
+        for (int g = 0; g < 8; ++g) yv[j][g] = *(const double2*)&sY[cur][(b0 + j) * 32 + 8 * (g >> 1) + 4 * h + 2 * (g & 1)];
+    };
+    if (gw) read_y(0);
     const double nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
     if (nrm2 == 0.0) break;  // C v = 0: keep the previous direction
     last = cur;
@@ -337,10 +357,17 @@ __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* s
     if (gw) {
       double part[NB];  // independent FMA chains, one per row block
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi) {
-        part[bi] = 0.0;
+      for (int b0 = 0; b0 < NB; b0 += YB) {
+        if (b0) read_y(b0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part[bi] = fma(cacc[bi][i], sY[cur][bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], part[bi]);
+        for (int j = 0; j < YB; ++j) {
+          part[b0 + j] = 0.0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const double2 y2 = yv[j][i >> 1];
+            part[b0 + j] = fma(cacc[b0 + j][i], (i & 1) ? y2.y : y2.x, part[b0 + j]);
+          }
+        }
       }
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) wv += part[bi];
@@ -426,16 +453,24 @@ __device__ __forceinline__ void project_rows(const void* Qv, size_t hbase, const
   using P = RowProjector<D, BF16>;
   P pr;
   pr.init(sV);
-  constexpr int U = 4;  // rows per lane group in flight
+  constexpr int U = 8;  // rows per lane group in flight
   const int w = wave_id(), sub = lane_id() / P::LPR;
   const int step = NT / 64 * P::RPW;
-  for (int b = r0 + w * P::RPW; b < r1; b += U * step) {
-    int id[U];
+  // the member ids of the next batch are loaded while this batch's rows are
+  // in flight, so each batch waits for one memory latency, not two
+  int id[U];
+  const int b0 = r0 + w * P::RPW;
 #pragma unroll
-    for (int u = 0; u < U; ++u) id[u] = nperm[min(b + u * step + sub, r1 - 1)];
+  for (int u = 0; u < U; ++u) id[u] = nperm[min(b0 + u * step + sub, r1 - 1)];
+  for (int b = b0; b < r1; b += U * step) {
     typename P::Row x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) x[u] = pr.load(Qv, hbase + id[u]);
+    const int bn = b + U * step;
+    if (bn < r1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) id[u] = nperm[min(bn + u * step + sub, r1 - 1)];
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = b + u * step + sub;
@@ -468,7 +503,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
   __shared__ __attribute__((aligned(1024))) unsigned char slotlo[L::SLOTLO];
   __shared__ __attribute__((aligned(16))) float sRf[D];
-  __shared__ double sS[D], sR[D], sV[D], sY[2][D], sRed[2][4];
+  __shared__ double sS[D], sR[D], sV[D], sRed[2][4];
+  __shared__ __attribute__((aligned(16))) double sY[2][D];
   __shared__ typename Sel::Shared sh;
   // the projection keys reuse the first tile slot once the scatter sums are
   // done (when they fit: d = 128)
@@ -482,8 +518,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   int32_t* nperm = p.perm + hbase + nd.start;
   if (BF16 && (int)threadIdx.x < D) sR[threadIdx.x] = (double)(float)((const __bf16*)p.Q)[(hbase + nperm[0]) * D + threadIdx.x];
   double cacc[D / 32][16];
-  gram_rows<D, BF16>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, slotlo, sRf, cacc, sS);  // its final barrier publishes sR
-  const double muv = centre_and_iterate<D>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
+  gram_rows<D, BF16, 2>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, slot1, slotlo, sRf, cacc, sS);  // its final barrier publishes sR
+  const double muv = centre_and_iterate<D, D / 64>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
   project_rows<D, BF16, kNodeThreads>(p.Q, hbase, nperm, 0, nd.n, sV, muv, [&](int i, uint32_t k) { s_keys[i] = k; });
   __syncthreads();
   Sel sel;
@@ -526,10 +562,11 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   using Sel = BlockSelect<kNodeThreads, VPT>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char slotlo[TILE];
   __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D], sR[D], sV[D], sMu[4];
-  __shared__ float sY[2][D], sRed[2][4];
+  __shared__ __attribute__((aligned(16))) float sY[2][D];
   __shared__ typename Sel::Shared sh;
   __shared__ uint32_t s_keys[kSmallRows];
   const int bh = blockIdx.y;
@@ -598,32 +635,36 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       accS = mfma_32x32x16(wl, ones, accS);
     }
   };
-  // tile t lands in its slot (double-buffered copies); after a barrier it is
-  // split in place (low parts in slotlo, single-buffered: every wave has
-  // finished the previous tile at that barrier), then, after another, used
+  // Tile t lands in slot t % 3 by copies issued two tiles ahead (ids loaded a
+  // tile before their copies); after a barrier it is split in place (low
+  // parts in slotlo, single-buffered: every wave has finished the previous
+  // tile at that barrier), then, after another, used.  When tile t is waited
+  // for, the loads issued after its copies are ids(t+1), the copies of t+1
+  // and ids(t+2).
+  unsigned char* const ring[3] = {slot0, slot1, slot2};
   load_ids(0);
-  issue(slot0);
-  if (ntiles > 1) load_ids(1);
-  for (int t = 0; t < ntiles; t += 2) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      issue(slot1);
-      if (t + 2 < ntiles) load_ids(t + 2);
+  issue(ring[0]);
+  if (ntiles > 1) {
+    load_ids(1);
+    issue(ring[1]);
+    if (ntiles > 2) load_ids(2);
+  }
+  for (int t0 = 0; t0 < ntiles; t0 += 3) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int t = t0 + k;
+      if (t >= ntiles) break;
+      if (t + 2 < ntiles) wait_vmcnt<3 * LPW>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (t + 2 < ntiles) {
+        issue(ring[(k + 2) % 3]);  // the slot of tile t-1, whose last reads ended before the barrier
+        if (t + 3 < ntiles) load_ids(t + 3);
+      }
+      split_tile<D, TR, kNodeThreads>(ring[k], slotlo, sRf);
+      __syncthreads();
+      compute(ring[k]);
     }
-    split_tile<D, TR, kNodeThreads>(slot0, slotlo, sRf);
-    __syncthreads();
-    compute(slot0);
-    if (t + 1 >= ntiles) break;
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (t + 2 < ntiles) {
-      issue(slot0);
-      if (t + 3 < ntiles) load_ids(t + 3);
-    }
-    split_tile<D, TR, kNodeThreads>(slot1, slotlo, sRf);
-    __syncthreads();
-    compute(slot1);
   }
   // column sums: lane (n, h) of wave w keeps element n%16: S[32w + 8((n%16)/4) + 4h + n%4]
   {
@@ -647,14 +688,38 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
         cf[bi][i] = (float)((double)acc[bi][i] - sS[bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)] * sc);
   }
   if (tid < D) sY[0][tid] = 1.0f / sqrtf((float)D);
-  if (tid < 4) sRed[0][tid] = tid == 0 ? 1.0f : 0.0f;
   __syncthreads();
+  // Every lane reads the rows 8g + 4h + 0..3 of each 32-row block of y, and
+  // its partner lane (h ^ 1) the others, so ||y||^2 is an in-lane sum plus
+  // one exchange, formed by every wave alike: no reduction across waves.  The
+  // step's scale 1/||y_k|| uses the hardware reciprocal square root (the
+  // direction does not depend on the scale; v is normalised in fp64 below).
+  auto read_y = [&](int buf, f32x4 (&yv)[NB][4]) {
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) yv[bi][g] = *(const f32x4*)&sY[buf][bi * 32 + 8 * g + 4 * h];
+  };
+  auto norm2 = [&](const f32x4 (&yv)[NB][4]) {
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = fmaf(yv[bi][g][e], yv[bi][g][e], q[e]);
+    return half_sum((q[0] + q[1]) + (q[2] + q[3]));
+  };
   int cur = 0, last = 0;
+  float nl = 1.0f;  // ||y_last||^2
   for (int it = 0; it < p.iters; ++it) {
-    const float nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
+    f32x4 yv[NB][4];
+    read_y(cur, yv);
+    const float nrm2 = norm2(yv);
     if (nrm2 == 0.0f) break;  // C v = 0: keep the previous direction
     last = cur;
-    const float inv = 1.0f / sqrtf(nrm2);
+    nl = nrm2;
+    const float inv = __builtin_amdgcn_rsqf(nrm2);
     float wv = 0.0f;
     if (gw) {
       float part[NB];
@@ -662,24 +727,26 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       for (int bi = 0; bi < NB; ++bi) {
         part[bi] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part[bi] = fmaf(cf[bi][i], sY[cur][bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)], part[bi]);
+        for (int i = 0; i < 16; ++i) part[bi] = fmaf(cf[bi][i], yv[bi][i >> 2][i & 3], part[bi]);
       }
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) wv += part[bi];
       wv = half_sum(wv) * inv;
     }
-    const float sq = wave_sum_f32((gw && h == 0) ? wv * wv : 0.0f);
     const int nxt = cur ^ 1;
     if (gw && h == 0) sY[nxt][w * 32 + ln] = wv;
-    if (l == 0 && w < 4) sRed[nxt][w] = gw ? sq : 0.0f;
     __syncthreads();
     cur = nxt;
   }
   {
-    const float nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
-    if (nrm2 != 0.0f) last = cur;
+    f32x4 yv[NB][4];
+    read_y(cur, yv);
+    const float nrm2 = norm2(yv);
+    if (nrm2 != 0.0f) {
+      last = cur;
+      nl = nrm2;
+    }
   }
-  const float nl = (sRed[last][0] + sRed[last][1]) + (sRed[last][2] + sRed[last][3]);
   const double vinv = 1.0 / sqrt((double)nl);
   if (tid < D) sV[tid] = (double)sY[last][tid] * vinv;
   __syncthreads();
@@ -713,18 +780,19 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   using L = GramLds<D, BF16>;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[L::SLOT0];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[L::SLOT1];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[L::SLOT2];
   __shared__ __attribute__((aligned(1024))) unsigned char slotlo[L::SLOTLO];
   __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D];
   const int bh = blockIdx.y, slot = blockIdx.x / p.pmax, chunk = blockIdx.x % p.pmax;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
   if (nd.c <= 1) return;
-  const int r0 = chunk * p.cr;
+  const int r0 = chunk * p.cg;
   if (r0 >= nd.n) return;
-  const int r1 = min(nd.n, r0 + p.cr);
+  const int r1 = min(nd.n, r0 + p.cg);
   const size_t hbase = (size_t)bh * p.Nq;
   double cacc[D / 32][16];
-  gram_rows<D, BF16>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, slotlo, sRf, cacc, sS);
+  gram_rows<D, BF16, 3>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, slot2, slotlo, sRf, cacc, sS);
   const int nslots = 1 << p.level;
   double* out = p.part + (((size_t)bh * nslots + slot) * p.pmax + chunk) * (D + D * D);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
@@ -747,7 +815,7 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   const int e = (blockIdx.x % RB) * 256 + threadIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
   if (nd.c <= 1 || e >= E) return;
-  const int parts = (nd.n + p.cr - 1) / p.cr;
+  const int parts = (nd.n + p.cg - 1) / p.cg;
   const size_t node = (size_t)bh * (1 << p.level) + slot;
   const double* src = p.part + node * p.pmax * E + e;
   // four partials loaded before they are added (four loads in flight), added in chunk order
@@ -767,7 +835,8 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
 template <int D, bool BF16>
 __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) {
   constexpr int E = D + D * D;
-  __shared__ double sS[D], sR[D], sV[D], sY[2][D], sRed[2][4];
+  __shared__ double sS[D], sR[D], sV[D], sRed[2][4];
+  __shared__ __attribute__((aligned(16))) double sY[2][D];
   const int bh = blockIdx.y, slot = blockIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
   if (nd.c <= 1) return;
@@ -787,7 +856,7 @@ __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) 
         cacc[bi][i] = red[D + (size_t)(32 * bi + 8 * (i >> 2) + 4 * h + (i & 3)) * D + 32 * w + ln];
   }
   __syncthreads();
-  const double muv = centre_and_iterate<D>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
+  const double muv = centre_and_iterate<D, D / 32>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
   double* out = p.vec + node * (D + 1);
   if (tid < D) out[tid] = sV[tid];
   if (tid == 0) out[D] = muv;
@@ -874,7 +943,7 @@ __global__ void pddp_init_kernel(int32_t* perm, int Nq, size_t total) {
 
 // Host-side plan: the tree's shape depends only on Nq and G.
 struct Plan {
-  int levels, cr;
+  int levels, cr, cg;
   size_t part, red, vec;  // doubles
 };
 
@@ -892,12 +961,15 @@ Plan make_plan(const Shape& s) {
   long long cr = ((long long)s.BH * s.Nq + 511) / 512;
   cr = (cr + 63) / 64 * 64;
   pl.cr = (int)(cr < 2048 ? 2048 : (cr > kMaxChunkRows ? kMaxChunkRows : cr));
+  // partial sums over chunks of cg rows: about 512 chunks over all heads at
+  // the top level (one round of two workgroups per CU), at least 512 rows each
+  pl.cg = (int)(cr < 512 ? 512 : (cr > pl.cr ? pl.cr : cr));
   const size_t E = (size_t)s.d + (size_t)s.d * s.d;
   for (int lv = 0; lv < pl.levels; ++lv) {
     const long long maxn = level_max_rows(s, lv);
     if (maxn <= pl.cr) break;
     const size_t nodes = (size_t)s.BH << lv;
-    const size_t pmax = (size_t)((maxn + pl.cr - 1) / pl.cr);
+    const size_t pmax = (size_t)((maxn + pl.cg - 1) / pl.cg);
     pl.part = std::max(pl.part, nodes * pmax * E);
     pl.red = std::max(pl.red, nodes * E);
     pl.vec = std::max(pl.vec, nodes * ((size_t)s.d + 1));
@@ -913,7 +985,7 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
     const int nslots = 1 << lv;
     const long long maxn = level_max_rows(s, lv);
     if (maxn > pl.cr) {
-      p.pmax = (int)((maxn + pl.cr - 1) / pl.cr);
+      p.pmax = (int)((maxn + pl.cg - 1) / pl.cg);
       const dim3 chunks(nslots * p.pmax, s.BH);
       hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
       hipLaunchKernelGGL((pddp_reduce_kernel<D>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
@@ -970,6 +1042,7 @@ hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, 
   p.G = s.G;
   p.iters = s.iters;
   p.cr = pl.cr;
+  p.cg = pl.cg;
   p.pmax = 1;
   hipLaunchKernelGGL(pddp_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, perm, s.Nq, n);
   if (bf16) {
