@@ -6,11 +6,10 @@
 // token-level KV selection is made.  (The gathered sparse attention of the
 // reuse step is in sparse_bf16.hip.)
 //
-// Shared structure of dense attention.  One wave owns 32 query rows.  K/V
-// tiles of 64 keys are staged in LDS: at d = 64 through registers into padded
-// rows (K rows padded so 16-lane 16-byte reads hit distinct banks, V rows
-// padded for the transposing reads), at d = 128 by direct-to-LDS copies into
-// the swizzled rows of ring.hpp.  Scores are formed transposed, S^T = K Q^T, with
+// Shared structure.  One wave owns 32 query rows.  K/V tiles of 64 keys are
+// staged in LDS (row-major; K rows padded so 16-lane 16-byte reads hit
+// distinct banks, V rows padded for the transposing reads) with a register
+// prefetch of the next tile.  Scores are formed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16, so each lane holds 32 keys of one query column:
 // the softmax max/sum are in-lane plus one exchange of the two wave halves,
 // and the probabilities already sit in the B-operand layout of the
@@ -154,13 +153,53 @@ struct Flash {
         }
   }
 
+  // 1 / row sum (0 for a row with no visible key) and the natural-log lse.
+  __device__ __forceinline__ float finish(float& lse) {
+    const float lt = half_sum(l_run);
+    lse = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -kInf;
+    return lt > 0.f ? 1.f / lt : 0.f;
+  }
 };
 
+// Output element (b, i) of a lane is d = b*32 + 8*(i/4) + 4*h + i%4: four
+// consecutive channels per (b, i/4).
+template <int D>
+__device__ __forceinline__ void store_row_bf16(__bf16* dst, const Flash<D>& st, float inv, const float* add) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = b * 32 + 8 * g + 4 * h;
+      f32x4 v = {st.acc[b][4 * g] * inv, st.acc[b][4 * g + 1] * inv, st.acc[b][4 * g + 2] * inv,
+                 st.acc[b][4 * g + 3] * inv};
+      if (add) v += *(const f32x4*)(add + d0);
+      bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      *(bf16x4*)(dst + d0) = o;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_row_f32(float* dst, const Flash<D>& st, float inv, bool subtract) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = b * 32 + 8 * g + 4 * h;
+      f32x4 v = {st.acc[b][4 * g] * inv, st.acc[b][4 * g + 1] * inv, st.acc[b][4 * g + 2] * inv,
+                 st.acc[b][4 * g + 3] * inv};
+      if (subtract) v = *(const f32x4*)(dst + d0) - v;
+      *(f32x4*)(dst + d0) = v;
+    }
+}
+
 // ---------------------------------------------------------------------------
-// Dense attention, natural token order: 256 queries (8 waves, 32 each) per
-// workgroup, so one staged K/V tile serves eight waves (against four: 6.80 ->
-// 6.39 ms at 32760 tokens, 12 heads, d = 128; 84.3 -> 80.1 ms at 131072
-// tokens, 16 heads, d = 64).
+// Dense attention, natural token order: 256 queries (8 waves) per workgroup,
+// so one staged K/V tile serves eight waves (against four: 6.80 -> 6.39 ms at
+// 32760 tokens, 12 heads, d = 128; 84.3 -> 80.1 ms at 131072 tokens, 16
+// heads, d = 64).  Two waves per SIMD at d = 128 (230 registers), four at
+// d = 64 (123).  Two LDS tiles, one barrier per tile.
 // ---------------------------------------------------------------------------
 struct DenseParams {
   const __bf16 *Q, *K, *V;
@@ -172,43 +211,15 @@ struct DenseParams {
   int causal_block, q_offset;
 };
 
-// Per-query outputs: O in bf16, optionally the fp32 O and the natural-log lse.
-template <int D>
-__device__ __forceinline__ void dense_store(const DenseParams& p, int bh, int q, const f32x16 (&acc)[D / 32],
-                                            float m_run, float l_run) {
-  const int h = lane_id() >> 5;
-  const float lt = half_sum(l_run);
-  const float lse = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -kInf;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (q >= p.Nq) return;
-  const size_t row = (size_t)bh * p.Nq + q;
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = b * 32 + 8 * g + 4 * h;
-      const f32x4 v = {acc[b][4 * g] * inv, acc[b][4 * g + 1] * inv, acc[b][4 * g + 2] * inv,
-                       acc[b][4 * g + 3] * inv};
-      const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-      *(bf16x4*)(p.O + row * D + d0) = o;
-      if (p.Ofull) *(f32x4*)(p.Ofull + row * D + d0) = v;
-    }
-  if (p.lse && h == 0) p.lse[row] = lse;
-}
-
-// Lock-step schedule (d = 64, four waves per SIMD): K/V tiles of 64 keys
-// staged through registers into padded LDS rows, two LDS tiles, one barrier
-// per tile; every wave runs the QK product, softmax and PV product of a tile
-// in turn.
 template <int D, int NW>
-__device__ __forceinline__ void dense_lockstep(const DenseParams& p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void dense_bf16_kernel(DenseParams p) {
   constexpr int NT = 64 * NW, QR = 32 * NW;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][64 * Tile<D>::KS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2][64 * Tile<D>::VS];
   const int unit = xcd_unit(blockIdx.x, p.per_xcd);
   if (unit >= p.n_units) return;
   const int bh = unit / p.n_qtiles, qt = unit - bh * p.n_qtiles;
-  const int w = wave_id(), n = lane_id() & 31;
+  const int w = wave_id(), n = lane_id() & 31, h = lane_id() >> 5;
   const int q = qt * QR + w * 32 + n;
   const bool qv = q < p.Nq;
   const int vcount = qv ? visible_limit(q, p.causal_block, p.q_offset, p.Nkv) : 0;
@@ -222,8 +233,9 @@ __device__ __forceinline__ void dense_lockstep(const DenseParams& p) {
   stage.load(Kh, Vh, 0, p.Nkv);
   stage.store(Ks[0], Vs[0]);
   __syncthreads();
-  // tile t + 1 is stored into the other buffer while tile t is used; the
-  // buffer written was last read before the previous barrier
+  // two LDS tiles: tile t + 1 is stored into the other buffer while tile t is
+  // used; one barrier per tile (the buffer written was last read before the
+  // previous barrier)
   for (int t = 0; t < ntiles; ++t) {
     const int base = t * 64, cur = t & 1;
     const bool more = t + 1 < ntiles;
@@ -232,260 +244,14 @@ __device__ __forceinline__ void dense_lockstep(const DenseParams& p) {
     if (more) stage.store(Ks[cur ^ 1], Vs[cur ^ 1]);
     __syncthreads();
   }
-  dense_store<D>(p, bh, q, st.acc, st.m_run, st.l_run);
-}
-
-// Ping-pong schedule (d = 128, two waves per SIMD).  The two waves that share
-// a SIMD belong to different groups, A and B.  Time is cut into slots by
-// workgroup barriers: in slot 2t group A runs the GEMM phase of tile t (the
-// PV product of tile t-1, then the QK product of tile t) while group B runs
-// the softmax of tile t-1; in slot 2t+1 A runs the softmax of tile t while B
-// runs the GEMM phase of tile t.  Each wave's arithmetic and its order are
-// those of the lock-step schedule, so the outputs are the same bits.  K/V
-// tiles of 64 keys arrive by direct-to-LDS copies into three unpadded,
-// swizzled buffers (the layout of ring.hpp), a tile ahead: every wave issues
-// its share of K(t+2) and V(t+1) at the start of slot 2t and waits for the
-// copies of the previous tile at the end of slot 2t+1.  Measured at 32760
-// tokens, 12 heads: 6.29-6.52 ms against 6.36-6.72 ms for the lock-step
-// schedule on the same boxes, and 1.09-1.15 against 1.24-1.29 ms for a
-// 4680-query frame-causal chunk; with the softmax removed the same
-// schedule runs at 3.2 ms (83 % of the bf16 peak), so the softmax phases are
-// what remains: they overlap the other group's MFMAs only in part.
-template <int D>
-struct PingPongWave {
-  static constexpr int NB = D / 32, NKS = D / 16;
-  static constexpr int ROWB = 2 * D, BLK = 32 * ROWB;
-  static constexpr int NPV = NB * 4, NMF = NPV + 2 * NKS;  // MFMAs of one GEMM phase
-  static constexpr int PF = 4;                             // operand reads run PF MFMAs ahead
-  bf16x8 qb[NKS];
-  f32x16 acc[NB];
-  f32x16 s[2];
-  bf16x8 pb[2][2];
-  float m_run, l_run;
-  int kbase, vbase0, vbase1;
-
-  __device__ __forceinline__ void init(const __bf16* qrow, bool valid) {
-    const int l = lane_id(), n = l & 31, h = l >> 5;
-    kbase = n * ROWB + 16 * (h ^ swz<D>(n));
-    const int vr = 4 * h + ((l & 15) >> 2);
-    const int c0 = 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
-    vbase0 = vr * ROWB + 8 * (l & 1) + 16 * (c0 ^ swz<D>(vr));
-    vbase1 = (8 + vr) * ROWB + 8 * (l & 1) + 16 * (c0 ^ swz<D>(8 + vr));
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 z = {};
-      qb[ks] = valid ? *(const bf16x8*)(qrow + ks * 16 + 8 * h) : z;
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-    s[0] = s[1] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) pb[kb][0] = pb[kb][1] = bf16x8{};
-    m_run = -kInf;
-    l_run = 0.f;
+  float lse;
+  const float inv = st.finish(lse);
+  if (qv) {
+    const size_t row = (size_t)bh * p.Nq + q;
+    store_row_bf16<D>(p.O + row * D, st, inv, nullptr);
+    if (p.Ofull) store_row_f32<D>(p.Ofull + row * D, st, inv, false);
+    if (p.lse && h == 0) p.lse[row] = lse;
   }
-
-  // A operand of MFMA i of the GEMM phase: i < NPV the V^T operand of the PV
-  // product (output block b, key block kb, k-step ks2), else the K operand of
-  // the QK product (key block kb, k-step ks).
-  __device__ __forceinline__ bf16x8 operand(int i, const unsigned char* Vs, const unsigned char* Ks) const {
-    if (i < NPV) {
-      const int b = i >> 2, kb = (i >> 1) & 1, ks2 = i & 1;
-      const int a0 = vbase0 ^ (64 * b), a1 = vbase1 ^ (64 * b);
-      const bf16x4 lo = lds_read_tr(Vs + kb * BLK + a0 + 16 * ROWB * ks2);
-      const bf16x4 hi = lds_read_tr(Vs + kb * BLK + a1 + 16 * ROWB * ks2);
-      return cat(lo, hi);
-    }
-    const int j = i - NPV, kb = j / NKS, ks = j % NKS;
-    return *(const bf16x8*)(Ks + kb * BLK + (kbase ^ (32 * ks)));
-  }
-
-  // O^T += V^T P^T of the previous tile (V rows at Vs), then S^T = K Q^T of
-  // this tile (K rows at Ks).
-  __device__ __forceinline__ void gemm(const unsigned char* Vs, const unsigned char* Ks) {
-    static_assert(NPV == 16 && NMF == 32 && PF == 4, "interleave below is written for d = 128");
-    bf16x8 op[PF + 2];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) op[i] = operand(i, Vs, Ks);
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      if (i + PF < NMF) op[(i + PF) % (PF + 2)] = operand(i + PF, Vs, Ks);
-      const bf16x8 a = op[i % (PF + 2)];
-      if (i < NPV) {
-        const int b = i >> 2, kb = (i >> 1) & 1, ks2 = i & 1;
-        acc[b] = mfma_32x32x16(a, pb[kb][ks2], acc[b]);
-      } else {
-        const int j = i - NPV, kb = j / NKS, ks = j % NKS;
-        s[kb] = mfma_32x32x16(a, qb[ks], ks ? s[kb] : f32x16{});
-      }
-    }
-    // keep the interleave: the LDS reads of MFMA i + PF right before MFMA i
-    // (two transposing reads per PV operand, one read per QK operand)
-#pragma unroll
-    for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < NPV - PF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-#pragma unroll
-    for (int i = NPV - PF; i < NMF - PF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-#pragma unroll
-    for (int i = NMF - PF; i < NMF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  }
-
-  // Softmax of the scores s of a tile whose first lim keys are visible: the
-  // probabilities (bf16) for the next PV product, the row sum, and O rescaled
-  // when the reference maximum moves (Flash<D>::tile's arithmetic).
-  __device__ __forceinline__ void softmax(int lim, float c) {
-    const int h = lane_id() >> 5;
-    if (lim < 64) {
-      const int lh = lim - 4 * h;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lh) s[kb][i] = -kInf;
-    }
-    float mx = -kInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = half_max(mx) * c;
-    const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
-    const float m_ref = (m_new == -kInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_ref);
-    m_run = m_new;
-    float ls4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[kb][i], c, -m_ref));
-        ls4[i & 3] += pv;
-        pb[kb][i >> 3][i & 7] = (__bf16)pv;
-      }
-    l_run = fmaf(l_run, alpha, (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] *= alpha;
-    }
-  }
-};
-
-// Workgroup barrier that the instruction scheduler may not move work across
-// (each phase's instructions stay in their slot).
-__device__ __forceinline__ void slot_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int D>
-__device__ __forceinline__ void dense_pingpong(const DenseParams& p) {
-  constexpr int QR = 256, TB = 64 * 2 * D;  // queries per workgroup, bytes of a K or V tile
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int CPW = CH / 8;               // wave-wide copies per wave per K or V tile
-  __shared__ __attribute__((aligned(1024))) unsigned char Kb[3][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vb[3][TB];
-  __shared__ int s_cnt[4];
-  const int unit = xcd_unit(blockIdx.x, p.per_xcd);
-  if (unit >= p.n_units) return;
-  const int bh = unit / p.n_qtiles, qt = unit - bh * p.n_qtiles;
-  const int w = wave_id(), l = lane_id(), n = l & 31;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  // group: the first wave of a SIMD to arrive is A, the second B (HW_ID bits
-  // 5:4 hold the SIMD)
-  if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0;
-  __syncthreads();
-  const int simd = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3;
-  int order = 0;
-  if (l == 0) order = atomicAdd(&s_cnt[simd], 1);
-  const bool grpA = __builtin_amdgcn_readfirstlane(order) == 0;
-  const int q = qt * QR + w * 32 + n;
-  const bool qv = q < p.Nq;
-  const int vcount = qv ? visible_limit(q, p.causal_block, p.q_offset, p.Nkv) : 0;
-  const int kmax = visible_limit(min(qt * QR + QR, p.Nq) - 1, p.causal_block, p.q_offset, p.Nkv);
-  const int T = (kmax + 63) / 64;
-  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.K + (size_t)bh * p.Nkv * D, p.Nkv * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.V + (size_t)bh * p.Nkv * D, p.Nkv * D * 2);
-  // copy j of this wave: 16-byte chunk ci = (wu*CPW + j)*64 + lane of the
-  // tile, row ci/CH, stored at chunk ci%CH (logical chunk (ci%CH) ^ swz(row));
-  // rows past the end of the head read as zeros (their keys are masked)
-  int coff[CPW];
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int ci = (wu * CPW + j) * 64 + l, r = ci / CH, pc = ci % CH;
-    coff[j] = r * 2 * D + 16 * (pc ^ swz<D>(r));
-  }
-  auto copy_k = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) dma16_buf(rk, t * TB + coff[j], Kb[t % 3] + (wu * CPW + j) * 1024);
-  };
-  auto copy_v = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) dma16_buf(rv, t * TB + coff[j], Vb[t % 3] + (wu * CPW + j) * 1024);
-  };
-  PingPongWave<D> st;
-  st.init(p.Q + ((size_t)bh * p.Nq + (qv ? q : 0)) * D, qv);
-  // V buffer 2 is "tile -1" of the first PV product: zeroed, so that with
-  // zero probabilities it adds exactly zero and every GEMM phase is the same
-  // code.  K(t) lives in Kb[t % 3], V(t - 1) in Vb[(t + 2) % 3].
-  for (int i = threadIdx.x; i < TB / 16; i += 512) *(u32x4*)(Vb[2] + 16 * i) = u32x4{0, 0, 0, 0};
-  if (T > 0) {
-    copy_k(0);
-    copy_v(0);
-  }
-  if (T > 1) copy_k(1);
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (grpA) {
-    for (int t = 0; t < T; ++t) {
-      const bool both = t + 2 < T;
-      if (t + 2 < T) copy_k(t + 2);
-      if (t + 1 < T) copy_v(t + 1);
-      st.gemm(Vb[(t + 2) % 3], Kb[t % 3]);
-      slot_barrier();
-      st.softmax(vcount - t * 64, p.c);
-      if (both) wait_vmcnt<2 * CPW>();
-      else wait_vmcnt<0>();
-      slot_barrier();
-    }
-    st.gemm(Vb[(T + 2) % 3], Kb[T % 3]);  // PV of the last tile (its QK result is unused)
-    slot_barrier();
-    slot_barrier();
-  } else {
-    if (2 < T) copy_k(2);
-    if (1 < T) copy_v(1);
-    slot_barrier();
-    st.gemm(Vb[2], Kb[0]);
-    if (2 < T) wait_vmcnt<2 * CPW>();
-    else wait_vmcnt<0>();
-    slot_barrier();
-    for (int t = 1; t <= T; ++t) {
-      const bool both = t + 2 < T;
-      if (t + 2 < T) copy_k(t + 2);
-      if (t + 1 < T) copy_v(t + 1);
-      st.softmax(vcount - (t - 1) * 64, p.c);
-      slot_barrier();
-      st.gemm(Vb[(t + 2) % 3], Kb[t % 3]);
-      if (both) wait_vmcnt<2 * CPW>();
-      else wait_vmcnt<0>();
-      slot_barrier();
-    }
-  }
-  dense_store<D>(p, bh, q, st.acc, st.m_run, st.l_run);
-}
-
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2, D == 64 ? 4 : 2))) void dense_bf16_kernel(DenseParams p) {
-  static_assert(D == 64 || NW == 8, "the ping-pong schedule is written for eight waves");
-  if constexpr (D == 128) dense_pingpong<D>(p);
-  else dense_lockstep<D, NW>(p);
 }
 
 // ---------------------------------------------------------------------------
