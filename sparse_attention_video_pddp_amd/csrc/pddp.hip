@@ -992,7 +992,17 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
       hipLaunchKernelGGL((pddp_power_kernel<D, BF16>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
       p.pj_pmax = (int)((maxn + kProjRows - 1) / kProjRows);
       hipLaunchKernelGGL((pddp_project_kernel<D, BF16>), dim3(nslots * p.pj_pmax, s.BH), dim3(256), 0, st, p);
-      if (maxn <= 64LL * kSplitThreads)
+      // the register cache sized to the node: the padding of a larger cache
+      // reads as key 0 and all of it lands in one histogram bin of the
+      // first radix pass (a 4096-row split in a 32768-key cache took as long
+      // as a 32768-row one)
+      if (maxn <= 8LL * kSplitThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 8>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+      else if (maxn <= 16LL * kSplitThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 16>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+      else if (maxn <= 32LL * kSplitThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 32>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+      else if (maxn <= 64LL * kSplitThreads)
         hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 64>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
       else if (maxn <= 80LL * kSplitWideThreads)
         hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 80>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
@@ -1006,6 +1016,8 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
         hipLaunchKernelGGL((pddp_small_kernel<D>), grid, dim3(kNodeThreads), 0, st, p);
       else if (maxn <= 2 * kNodeThreads)
         hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 2>), grid, dim3(kNodeThreads), 0, st, p);
+      else if (maxn <= 4 * kNodeThreads)
+        hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 4>), grid, dim3(kNodeThreads), 0, st, p);
       else if (maxn <= 8 * kNodeThreads)
         hipLaunchKernelGGL((pddp_node_kernel<D, BF16, 8>), grid, dim3(kNodeThreads), 0, st, p);
       else
