@@ -15,6 +15,8 @@
 // and the probabilities already sit in the B-operand layout of the
 // O^T = V^T P^T product (the A operand V^T comes from ds_read_b64_tr_b16).
 // Online softmax runs in base 2 with scale*log2(e) folded into one FMA.
+#include <type_traits>
+
 #include "mcs_kernels.hpp"
 #include "ring.hpp"
 
@@ -88,6 +90,10 @@ struct Flash {
 
   // One 64-key tile.  lim: how many leading keys of the tile are visible to
   // this lane's query (any integer; >= 64 means all).  c = scale*log2(e).
+  // MASK = false: every key of the tile is visible to every query of the
+  // wave (no masking code, so nothing divergent separates the QK MFMAs from
+  // the maximum).
+  template <bool MASK>
   __device__ __forceinline__ void tile(const __bf16* Ks, const __bf16* Vs, int lim, float c) {
     const int l = lane_id(), n = l & 31, h = l >> 5;
     f32x16 s[2];
@@ -100,7 +106,7 @@ struct Flash {
         s[kb] = mfma_32x32x16(a, qb[ks], s[kb]);
       }
     }
-    if (lim < 64) {
+    if (MASK && lim < 64) {
       const int lh = lim - 4 * h;  // element i of block kb is key kb*32 + 8*(i/4) + 4*h + i%4
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -151,6 +157,10 @@ struct Flash {
           acc[b] = mfma_32x32x16(cat(lds_read_tr(vp), lds_read_tr(vp + 8 * Tile<D>::VS)), pb[kb][ks2],
                                  acc[b]);
         }
+    // the row-sum update stays in this block, beside the PV MFMAs (left to
+    // itself the compiler sinks it past the next tile's LDS stores, where it
+    // issues alone)
+    asm volatile("" : "+v"(l_run));
   }
 
   // 1 / row sum (0 for a row with no visible key) and the natural-log lse.
@@ -236,14 +246,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
   // two LDS tiles: tile t + 1 is stored into the other buffer while tile t is
   // used; one barrier per tile (the buffer written was last read before the
   // previous barrier)
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](int t, auto maskc) {
     const int base = t * 64, cur = t & 1;
     const bool more = t + 1 < ntiles;
     if (more) stage.load(Kh, Vh, base + 64, p.Nkv - base - 64);
-    st.tile(Ks[cur], Vs[cur], vcount - base, p.c);
+    st.template tile<decltype(maskc)::value>(Ks[cur], Vs[cur], vcount - base, p.c);
     if (more) stage.store(Ks[cur ^ 1], Vs[cur ^ 1]);
     __syncthreads();
-  }
+  };
+  // the first nfull tiles are visible in full to every query of the
+  // workgroup (its first query sees the fewest keys) and need no masking:
+  // 6.25 -> 6.00 ms at 32760 tokens, 12 heads; 1.12 -> 0.92 ms for a
+  // frame-causal chunk of 4680 queries over 32760 keys
+  const int nfull = min(ntiles, visible_limit(min(qt * QR, p.Nq - 1), p.causal_block, p.q_offset, p.Nkv) / 64);
+  int t = 0;
+  for (; t < nfull; ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
   float lse;
   const float inv = st.finish(lse);
   if (qv) {
