@@ -216,33 +216,50 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     // one fp32 accumulator live at a time (row blocks outer), which keeps the
     // kernel within 256 registers per lane (a chain of dependent MFMAs issues
     // as fast as independent ones); y y^T = (hi + lo)(hi + lo)^T as four exact
-    // products
-    auto compute = [&](const unsigned char* slot) {
-      if (w >= NB) return;
-      f32x16 accS = {};
+    // products.  Block (a, c): rows of channel block a, columns of block c.
+    auto block = [&](const unsigned char* slot, int a, int c, bool sums, f32x16& accS) {
+      f32x16 acc = {};
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2) {
-          const bf16x8 wh = operand(slot, w, ks2), wl = operand(slotlo, w, ks2);
-          const bf16x8 hb = operand(slot, bi, ks2), lb = operand(slotlo, bi, ks2);
-          acc = mfma_32x32x16(hb, wh, acc);
-          acc = mfma_32x32x16(hb, wl, acc);
-          acc = mfma_32x32x16(lb, wh, acc);
-          acc = mfma_32x32x16(lb, wl, acc);
-          if (bi == 0) {
-            accS = mfma_32x32x16(wh, ones, accS);
-            accS = mfma_32x32x16(wl, ones, accS);
-          }
+      for (int ks2 = 0; ks2 < 4; ++ks2) {
+        const bf16x8 wh = operand(slot, c, ks2), wl = operand(slotlo, c, ks2);
+        const bf16x8 hb = operand(slot, a, ks2), lb = operand(slotlo, a, ks2);
+        acc = mfma_32x32x16(hb, wh, acc);
+        acc = mfma_32x32x16(hb, wl, acc);
+        acc = mfma_32x32x16(lb, wh, acc);
+        acc = mfma_32x32x16(lb, wl, acc);
+        if (sums) {
+          accS = mfma_32x32x16(wh, ones, accS);
+          accS = mfma_32x32x16(wl, ones, accS);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) cacc[bi][i] += (double)acc[i];
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cacc[a][i] += (double)acc[i];
+    };
+    auto add_sums = [&](const f32x16& accS) {
       float sv = accS[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) sv = (si == i) ? accS[i] : sv;
       sacc += (double)sv;
+    };
+    // d = 64: wave w < 2 forms both blocks of its column
+    auto compute = [&](const unsigned char* slot) {
+      if (w >= NB) return;
+      f32x16 accS = {};
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) block(slot, bi, w, bi == 0, accS);
+      add_sums(accS);
+    };
+    // d = 128: the matrix is symmetric, so only ten of its sixteen blocks are
+    // formed: wave W the blocks (W, W), (W+1, W) and, for W < 2, (W+2, W)
+    // (indices mod 4), all in its own column; the blocks of its column formed
+    // by other waves arrive transposed through LDS after the last tile
+    auto compute_sym = [&](const unsigned char* slot, auto wc) {
+      constexpr int W = decltype(wc)::value;
+      f32x16 accS = {};
+      block(slot, W, W, true, accS);
+      block(slot, (W + 1) & 3, W, false, accS);
+      if constexpr (W < 2) block(slot, W + 2, W, false, accS);
+      add_sums(accS);
     };
     static_assert(NS == 2 || NS == 3, "ring depth");
     unsigned char* const ring[3] = {slot0, slot1, slot2};
@@ -259,22 +276,77 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     }
     if (NS - 1 < ntiles) load_ids(NS - 1);
     // unrolled by NS so that every slot address is a constant of its copy
-    for (int t0 = 0; t0 < ntiles; t0 += NS) {
+    auto tiles = [&](auto cf) {
+      for (int t0 = 0; t0 < ntiles; t0 += NS) {
 #pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const int t = t0 + k;
-        if (t >= ntiles) break;
-        if (t + NS - 1 < ntiles) wait_vmcnt<(2 * NS - 3) * C::LPW>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        if (t + NS - 1 < ntiles) {
-          issue(ring[(k + NS - 1) % NS]);  // the slot of tile t-1, whose last reads ended before the barrier
-          if (t + NS < ntiles) load_ids(t + NS);
+        for (int k = 0; k < NS; ++k) {
+          const int t = t0 + k;
+          if (t >= ntiles) break;
+          if (t + NS - 1 < ntiles) wait_vmcnt<(2 * NS - 3) * C::LPW>();
+          else wait_vmcnt<0>();
+          __syncthreads();
+          if (t + NS - 1 < ntiles) {
+            issue(ring[(k + NS - 1) % NS]);  // the slot of tile t-1, whose last reads ended before the barrier
+            if (t + NS < ntiles) load_ids(t + NS);
+          }
+          split_tile<D, 64, 256>(ring[k], slotlo, sRf);
+          __syncthreads();
+          cf(ring[k]);
         }
-        split_tile<D, 64, 256>(ring[k], slotlo, sRf);
-        __syncthreads();
-        compute(ring[k]);
       }
+    };
+    if constexpr (NB == 4) {
+      // 32x32 fp64 blocks exchanged through the tile slots (free after the
+      // last tile): block m holds wave m's (m+1, m) block for m < 4 and wave
+      // m-4's (m-2, m-4) block for m = 4, 5; element (r, c) at r*32 + (c ^ r)
+      // (conflict-free both for the row-wise stores and the column-wise reads)
+      auto xblk = [&](int m) {
+        return (double*)(m < 2 ? slot0 + m * 8192 : (m < 4 ? slot1 + (m - 2) * 8192 : slotlo + (m - 4) * 8192));
+      };
+      auto run = [&](auto wc) {
+        constexpr int W = decltype(wc)::value;
+        tiles([&](const unsigned char* slot) { compute_sym(slot, wc); });
+        __syncthreads();  // every operand read of the last tile is done
+        auto put = [&](int m, int a) {
+          double* X = xblk(m);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+            X[r * 32 + (ln ^ r)] = cacc[a][i];
+          }
+        };
+        put(W, (W + 1) & 3);
+        if constexpr (W < 2) put(4 + W, W + 2);
+        __syncthreads();
+        // block (bi, W) of this column is the transpose of block (W, bi),
+        // formed by wave bi
+        auto get = [&](int m, int bi) {
+          const double* X = xblk(m);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+            cacc[bi][i] = X[ln * 32 + (r ^ ln)];
+          }
+        };
+        if constexpr (W == 0) get(3, 3);
+        if constexpr (W == 1) get(0, 0);
+        if constexpr (W == 2) {
+          get(4, 0);
+          get(1, 1);
+        }
+        if constexpr (W == 3) {
+          get(5, 1);
+          get(2, 2);
+        }
+      };
+      switch (__builtin_amdgcn_readfirstlane(w)) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        default: run(std::integral_constant<int, 3>{}); break;
+      }
+    } else {
+      tiles(compute);
     }
     if (w < NB && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = sacc;
     __syncthreads();
@@ -613,27 +685,32 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   f32x16 acc[NB], accS = {};
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-  // y^T operands from the split tile (hi part in the slot, lo part in slotlo)
-  auto compute = [&](const unsigned char* slot) {
-    if (!gw) return;
+  // y^T operands from the split tile (hi part in the slot, lo part in slotlo);
+  // the blocks (a, c) with a in rows, c in columns, formed for every a in `as`
+  auto compute_blocks = [&](const unsigned char* slot, int c, auto... as) {
 #pragma unroll
     for (int ks2 = 0; ks2 < TR / 16; ++ks2) {
       auto part = [&](const unsigned char* t, int b) {
         const unsigned char* base = t + 16 * (2 * D) * ks2;
         return cat(lds_read_tr(base + (ob0 ^ (64 * b))), lds_read_tr(base + (ob1 ^ (64 * b))));
       };
-      const bf16x8 wh = part(slot, w), wl = part(slotlo, w);  // this wave's column block
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi) {
+      const bf16x8 wh = part(slot, c), wl = part(slotlo, c);  // the column block
+      auto one = [&](int bi) {
         const bf16x8 hb = part(slot, bi), lb = part(slotlo, bi);
         acc[bi] = mfma_32x32x16(hb, wh, acc[bi]);
         acc[bi] = mfma_32x32x16(hb, wl, acc[bi]);
         acc[bi] = mfma_32x32x16(lb, wh, acc[bi]);
         acc[bi] = mfma_32x32x16(lb, wl, acc[bi]);
-      }
+      };
+      (one(as), ...);
       accS = mfma_32x32x16(wh, ones, accS);
       accS = mfma_32x32x16(wl, ones, accS);
     }
+  };
+  // d = 64: wave w < 2 forms both blocks of its column
+  auto compute = [&](const unsigned char* slot) {
+    if (!gw) return;
+    compute_blocks(slot, w, 0, 1);
   };
   // Tile t lands in slot t % 3 by copies issued two tiles ahead (ids loaded a
   // tile before their copies); after a barrier it is split in place (low
@@ -649,22 +726,76 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
     issue(ring[1]);
     if (ntiles > 2) load_ids(2);
   }
-  for (int t0 = 0; t0 < ntiles; t0 += 3) {
+  auto tiles = [&](auto cf) {
+    for (int t0 = 0; t0 < ntiles; t0 += 3) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int t = t0 + k;
-      if (t >= ntiles) break;
-      if (t + 2 < ntiles) wait_vmcnt<3 * LPW>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-      if (t + 2 < ntiles) {
-        issue(ring[(k + 2) % 3]);  // the slot of tile t-1, whose last reads ended before the barrier
-        if (t + 3 < ntiles) load_ids(t + 3);
+      for (int k = 0; k < 3; ++k) {
+        const int t = t0 + k;
+        if (t >= ntiles) break;
+        if (t + 2 < ntiles) wait_vmcnt<3 * LPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (t + 2 < ntiles) {
+          issue(ring[(k + 2) % 3]);  // the slot of tile t-1, whose last reads ended before the barrier
+          if (t + 3 < ntiles) load_ids(t + 3);
+        }
+        split_tile<D, TR, kNodeThreads>(ring[k], slotlo, sRf);
+        __syncthreads();
+        cf(ring[k]);
       }
-      split_tile<D, TR, kNodeThreads>(ring[k], slotlo, sRf);
-      __syncthreads();
-      compute(ring[k]);
     }
+  };
+  if constexpr (NB == 4) {
+    // d = 128: the scatter matrix is symmetric, so wave W forms only the
+    // blocks (W, W), (W+1, W) and, for W < 2, (W+2, W) (indices mod 4) of its
+    // column; the other blocks of its column arrive transposed through the
+    // tile slots after the last tile (fp32 32x32 blocks, element (r, c) at
+    // r*32 + (c ^ r): block m holds wave m's (m+1, m) block for m < 4 and
+    // wave m-4's (m-2, m-4) block for m = 4, 5)
+    auto xblk = [&](int m) { return (float*)(m < 4 ? ring[m >> 1] + (m & 1) * 4096 : slotlo + (m - 4) * 4096); };
+    auto run = [&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      if constexpr (W < 2) tiles([&](const unsigned char* slot) { compute_blocks(slot, W, W, (W + 1) & 3, W + 2); });
+      else tiles([&](const unsigned char* slot) { compute_blocks(slot, W, W, (W + 1) & 3); });
+      __syncthreads();  // every operand read of the last tile is done
+      auto put = [&](int m, int a) {
+        float* X = xblk(m);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+          X[r * 32 + (ln ^ r)] = acc[a][i];
+        }
+      };
+      put(W, (W + 1) & 3);
+      if constexpr (W < 2) put(4 + W, W + 2);
+      __syncthreads();
+      auto get = [&](int m, int bi) {
+        const float* X = xblk(m);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+          acc[bi][i] = X[ln * 32 + (r ^ ln)];
+        }
+      };
+      if constexpr (W == 0) get(3, 3);
+      if constexpr (W == 1) get(0, 0);
+      if constexpr (W == 2) {
+        get(4, 0);
+        get(1, 1);
+      }
+      if constexpr (W == 3) {
+        get(5, 1);
+        get(2, 2);
+      }
+    };
+    switch (wu) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      default: run(std::integral_constant<int, 3>{}); break;
+    }
+  } else {
+    tiles(compute);
   }
   // column sums: lane (n, h) of wave w keeps element n%16: S[32w + 8((n%16)/4) + 4h + n%4]
   {
