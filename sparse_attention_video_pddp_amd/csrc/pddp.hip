@@ -36,7 +36,8 @@
 // small-node kernel's 32-row tiles), row-major with the 16-byte chunks
 // XOR-swizzled per row; both MFMA operands (x^T blocks) are read with
 // ds_read_b64_tr_b16.  The partial sums of the many-workgroup levels cover
-// chunks of cg rows, about 512 chunks over all heads at the top level.  Wave w holds column block w of the scatter
+// chunks of cg rows, set per level so that a level has at most 512 chunks over
+// all heads (one round of two workgroups per CU).  Wave w holds column block w of the scatter
 // matrix in the MFMA output layout (lane: one column, 16 rows per 32-row
 // block), so C v needs only an in-lane sum and one half-wave exchange.
 #include <algorithm>
@@ -1074,9 +1075,22 @@ __global__ void pddp_init_kernel(int32_t* perm, int Nq, size_t total) {
 
 // Host-side plan: the tree's shape depends only on Nq and G.
 struct Plan {
-  int levels, cr, cg;
+  int levels, cr;
   size_t part, red, vec;  // doubles
 };
+
+// Rows per partial scatter sum at a many-workgroup level: as many chunks per
+// node as keep the level's chunks within one round of two gram workgroups
+// per CU (512 on 256 CUs), at least 512 rows each.  (A fixed chunk of
+// BH*Nq/512 rows gave every level a few more than 512 chunks, so each gram
+// launch ran a second, almost empty round: twice its time.)
+constexpr int kGramSlots = 512;
+long long gram_chunk_rows(long long maxn, int BH, int nslots) {
+  const long long per_node = std::max(1LL, (long long)kGramSlots / ((long long)BH * nslots));
+  long long cg = (maxn + per_node - 1) / per_node;
+  cg = (cg + 63) / 64 * 64;
+  return cg < 512 ? 512 : cg;
+}
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -1092,15 +1106,13 @@ Plan make_plan(const Shape& s) {
   long long cr = ((long long)s.BH * s.Nq + 511) / 512;
   cr = (cr + 63) / 64 * 64;
   pl.cr = (int)(cr < 2048 ? 2048 : (cr > kMaxChunkRows ? kMaxChunkRows : cr));
-  // partial sums over chunks of cg rows: about 512 chunks over all heads at
-  // the top level (one round of two workgroups per CU), at least 512 rows each
-  pl.cg = (int)(cr < 512 ? 512 : (cr > pl.cr ? pl.cr : cr));
   const size_t E = (size_t)s.d + (size_t)s.d * s.d;
   for (int lv = 0; lv < pl.levels; ++lv) {
     const long long maxn = level_max_rows(s, lv);
     if (maxn <= pl.cr) break;
     const size_t nodes = (size_t)s.BH << lv;
-    const size_t pmax = (size_t)((maxn + pl.cg - 1) / pl.cg);
+    const long long cg = gram_chunk_rows(maxn, s.BH, 1 << lv);
+    const size_t pmax = (size_t)((maxn + cg - 1) / cg);
     pl.part = std::max(pl.part, nodes * pmax * E);
     pl.red = std::max(pl.red, nodes * E);
     pl.vec = std::max(pl.vec, nodes * ((size_t)s.d + 1));
@@ -1116,7 +1128,8 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
     const int nslots = 1 << lv;
     const long long maxn = level_max_rows(s, lv);
     if (maxn > pl.cr) {
-      p.pmax = (int)((maxn + pl.cg - 1) / pl.cg);
+      p.cg = (int)gram_chunk_rows(maxn, s.BH, nslots);
+      p.pmax = (int)((maxn + p.cg - 1) / p.cg);
       const dim3 chunks(nslots * p.pmax, s.BH);
       hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
       hipLaunchKernelGGL((pddp_reduce_kernel<D>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
@@ -1185,7 +1198,6 @@ hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, 
   p.G = s.G;
   p.iters = s.iters;
   p.cr = pl.cr;
-  p.cg = pl.cg;
   p.pmax = 1;
   hipLaunchKernelGGL(pddp_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, perm, s.Nq, n);
   if (bf16) {
