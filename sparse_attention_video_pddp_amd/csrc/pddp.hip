@@ -158,7 +158,18 @@ struct GramLds {
 // 4*h + i%4, column 32*w + lane%32.  sS[0..D): sum y.  For bf16 rows
 // y = x - Q[nperm[0]] (the node's first member row), for fp32 rows y = x.
 // Ends with a barrier.
-template <int D, bool BF16, int NS>
+// Partial sums of the many-workgroup levels: S (D doubles), then the
+// scatter matrix.  bf16 rows at d = 128 form only the ten blocks of one
+// triangle (gram_rows), stored as ten 32x32 blocks in the MFMA output layout
+// (element i of lane l at i*64 + l): block m = W is (W, W), m = 4 + W is
+// (W+1 mod 4, W), m = 8 + W is (W+2, W) for W < 2 (rows, columns).  Other
+// inputs store the full matrix, row-major.
+template <int D, bool BF16>
+constexpr bool kSymPart = BF16 && D == 128;
+template <int D, bool BF16>
+constexpr int kPartE = kSymPart<D, BF16> ? D + 10 * 1024 : D + D * D;
+
+template <int D, bool BF16, int NS, bool XCH = true>
 __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
                           unsigned char* slot0, unsigned char* slot1, unsigned char* slot2, unsigned char* slotlo,
                           float* sRf, double (&cacc)[D / 32][16], double* sS) {
@@ -307,6 +318,7 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
       auto run = [&](auto wc) {
         constexpr int W = decltype(wc)::value;
         tiles([&](const unsigned char* slot) { compute_sym(slot, wc); });
+        if constexpr (!XCH) return;  // the caller stores the formed blocks as they are
         __syncthreads();  // every operand read of the last tile is done
         auto put = [&](int m, int a) {
           double* X = xblk(m);
@@ -924,12 +936,26 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   const int r1 = min(nd.n, r0 + p.cg);
   const size_t hbase = (size_t)bh * p.Nq;
   double cacc[D / 32][16];
-  gram_rows<D, BF16, 3>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, slot2, slotlo, sRf, cacc, sS);
+  constexpr int E = kPartE<D, BF16>;
+  gram_rows<D, BF16, 3, !kSymPart<D, BF16>>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, slot2, slotlo,
+                                            sRf, cacc, sS);
   const int nslots = 1 << p.level;
-  double* out = p.part + (((size_t)bh * nslots + slot) * p.pmax + chunk) * (D + D * D);
+  double* out = p.part + (((size_t)bh * nslots + slot) * p.pmax + chunk) * E;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
   if (tid < D) out[tid] = sS[tid];
-  if (w < D / 32) {
+  if constexpr (kSymPart<D, BF16>) {
+    // the blocks this wave formed (see kPartE)
+    auto put = [&](int m, int a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out[D + m * 1024 + i * 64 + l] = cacc[a][i];
+    };
+    switch (__builtin_amdgcn_readfirstlane(w)) {
+      case 0: put(0, 0); put(4, 1); put(8, 2); break;
+      case 1: put(1, 1); put(5, 2); put(9, 3); break;
+      case 2: put(2, 2); put(6, 3); break;
+      default: put(3, 3); put(7, 0); break;
+    }
+  } else if (w < D / 32) {
 #pragma unroll
     for (int bi = 0; bi < D / 32; ++bi)
 #pragma unroll
@@ -939,9 +965,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 // Ordered sum of a node's partials (same order on every run).
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
-  constexpr int E = D + D * D;
+  constexpr int E = kPartE<D, BF16>;
   constexpr int RB = (E + 255) / 256;
   const int bh = blockIdx.y, slot = blockIdx.x / RB;
   const int e = (blockIdx.x % RB) * 256 + threadIdx.x;
@@ -966,8 +992,9 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) {
-  constexpr int E = D + D * D;
+  constexpr int E = kPartE<D, BF16>;
   __shared__ double sS[D], sR[D], sV[D], sRed[2][4];
+  __shared__ double sX[kSymPart<D, BF16> ? 4 : 1][2][kSymPart<D, BF16> ? 1024 : 1];
   __shared__ __attribute__((aligned(16))) double sY[2][D];
   const int bh = blockIdx.y, slot = blockIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
@@ -980,7 +1007,37 @@ __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) 
   // the shift of the partial sums: the node's first member row (bf16 inputs)
   const size_t hbase = (size_t)bh * p.Nq;
   if (BF16 && tid < D) sR[tid] = (double)(float)((const __bf16*)p.Q)[(hbase + p.perm[hbase + nd.start]) * D + tid];
-  if (w < D / 32) {
+  if constexpr (kSymPart<D, BF16>) {
+    // block (bi, W) of column W: stored as it is, or as the transpose of the
+    // stored block (W, bi); element (r, c) of a stored block sits at
+    // i*64 + l with r = 8*(i/4) + 4*(l/32) + i%4, c = l%32
+    auto direct = [&](int bi, int m) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cacc[bi][i] = red[D + m * 1024 + i * 64 + l];
+    };
+    // a transposed block passes through this wave's own LDS area (coalesced
+    // global reads; element (r, c) at r*32 + (c ^ r), conflict-free both ways)
+    auto transposed = [&](int bi, int m, int k) {
+      double* X = sX[w][k];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        X[r * 32 + (ln ^ r)] = red[D + m * 1024 + i * 64 + l];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // other lanes' stores before these reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        cacc[bi][i] = X[ln * 32 + (r ^ ln)];
+      }
+    };
+    switch (__builtin_amdgcn_readfirstlane(w)) {
+      case 0: direct(0, 0); direct(1, 4); direct(2, 8); transposed(3, 7, 0); break;
+      case 1: direct(1, 1); direct(2, 5); direct(3, 9); transposed(0, 4, 0); break;
+      case 2: direct(2, 2); direct(3, 6); transposed(0, 8, 0); transposed(1, 5, 1); break;
+      default: direct(3, 3); direct(0, 7); transposed(1, 9, 0); transposed(2, 6, 1); break;
+    }
+  } else if (w < D / 32) {
 #pragma unroll
     for (int bi = 0; bi < D / 32; ++bi)
 #pragma unroll
@@ -1122,7 +1179,7 @@ Plan make_plan(const Shape& s) {
 
 template <int D, bool BF16>
 void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st) {
-  constexpr int RB = (D + D * D + 255) / 256;
+  constexpr int RB = (kPartE<D, BF16> + 255) / 256;
   for (int lv = 0; lv < pl.levels; ++lv) {
     p.level = lv;
     const int nslots = 1 << lv;
@@ -1132,7 +1189,7 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
       p.pmax = (int)((maxn + p.cg - 1) / p.cg);
       const dim3 chunks(nslots * p.pmax, s.BH);
       hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
-      hipLaunchKernelGGL((pddp_reduce_kernel<D>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((pddp_reduce_kernel<D, BF16>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
       hipLaunchKernelGGL((pddp_power_kernel<D, BF16>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
       p.pj_pmax = (int)((maxn + kProjRows - 1) / kProjRows);
       hipLaunchKernelGGL((pddp_project_kernel<D, BF16>), dim3(nslots * p.pj_pmax, s.BH), dim3(256), 0, st, p);
