@@ -625,17 +625,17 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 
 // ---- small nodes ------------------------------------------------------------
 // Nodes of at most kSmallRows rows (the deep levels: thousands of nodes, each a
-// chain of latencies) run with a lighter state so that four workgroups share a
-// CU: the scatter sums of the shifted rows y = x - r (r: the node's first
-// member row; y = hi + lo in two bf16 parts, see split_shifted) stay in the
-// fp32 MFMA accumulators over all tiles (exact products, fp32 sums over at
-// most kSmallRows rows), the centring is done in fp64 and the power iteration
-// runs in fp32 (C rounded to fp32); the projections stay fp64.  Row tiles of
-// 32 rows in a two-slot ring of 8 KB.
+// chain of latencies) run with a lighter state so that more workgroups share
+// a CU (three at d = 128, four at d = 64): the scatter sums of the shifted
+// rows y = x - r (r: the node's first member row; y = hi + lo in two bf16
+// parts, see split_shifted) stay in the fp32 MFMA accumulators over all tiles
+// (exact products, fp32 sums over at most kSmallRows rows), the centring is
+// done in fp64 and the power iteration runs in fp32 (C rounded to fp32); the
+// projections stay fp64.  Row tiles of 32 rows in a three-slot ring.
 constexpr int kSmallRows = 512;
 
 template <int D>
-__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void pddp_small_kernel(PddpParams p) {
+__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3))) void pddp_small_kernel(PddpParams p) {
   constexpr int NB = D / 32;
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int RPL = 64 / CH;         // rows per wave-wide copy
@@ -645,14 +645,20 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   constexpr int VPT = kSmallRows / kNodeThreads;
   static_assert(LPW >= 1, "tile copy split");
   using Sel = BlockSelect<kNodeThreads, VPT>;
-  __shared__ __attribute__((aligned(1024))) unsigned char slot0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot1[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot2[TILE];
+  // at d = 128 the block select's tables share the ring slots, which are
+  // free once the scatter sums are formed (39 KB of LDS: three workgroups per
+  // CU instead of two)
+  constexpr bool kShInSlots = sizeof(typename Sel::Shared) <= 3 * TILE;
+  __shared__ __attribute__((aligned(1024))) unsigned char slots[3 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char slotlo[TILE];
+  __shared__ typename Sel::Shared sh_own[1];  // d = 64 only (removed when unused)
+  unsigned char* const slot0 = slots;
+  unsigned char* const slot1 = slots + TILE;
+  unsigned char* const slot2 = slots + 2 * TILE;
+  typename Sel::Shared& sh = kShInSlots ? *reinterpret_cast<typename Sel::Shared*>(slots) : sh_own[0];
   __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D], sR[D], sV[D], sMu[4];
   __shared__ __attribute__((aligned(16))) float sY[2][D];
-  __shared__ typename Sel::Shared sh;
   __shared__ uint32_t s_keys[kSmallRows];
   const int bh = blockIdx.y;
   const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
