@@ -52,7 +52,7 @@ namespace {
 
 constexpr int kNodeThreads = 256;
 constexpr int kSplitThreads = 512;
-constexpr int kSplitWideThreads = 1024;  // nodes of 32769..81920 rows: 80 keys per thread
+constexpr int kSplitWideThreads = 1024;  // nodes of 8193..81920 rows
 constexpr int kProjRows = 512;      // rows per workgroup of the projection kernel
 constexpr int kMaxChunkRows = 4096;  // row chunk of the many-workgroup levels; larger nodes split there
 
@@ -1203,14 +1203,18 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
       // reads as key 0 and all of it lands in one histogram bin of the
       // first radix pass (a 4096-row split in a 32768-key cache took as long
       // as a 32768-row one)
+      // (1024 threads from 8193 keys on: the top levels run only a few of
+      // these workgroups)
       if (maxn <= 8LL * kSplitThreads)
         hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 8>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
       else if (maxn <= 16LL * kSplitThreads)
         hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 16>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
-      else if (maxn <= 32LL * kSplitThreads)
-        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 32>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
-      else if (maxn <= 64LL * kSplitThreads)
-        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 64>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+      else if (maxn <= 16LL * kSplitWideThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 16>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
+                           st, p);
+      else if (maxn <= 32LL * kSplitWideThreads)
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 32>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
+                           st, p);
       else if (maxn <= 80LL * kSplitWideThreads)
         hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 80>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
                            st, p);
