@@ -524,8 +524,15 @@ struct RowProjector {
 #pragma unroll
       for (int j = 0; j < 4; ++j) d = fma((double)r.x[1][j], vv[4 + j], d);
     }
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o, 64);
+    // sum over the row's LPR lanes (8 or 16, aligned) by DPP moves: quad
+    // swaps, then the half-row and row mirrors (every lane of a quad holds the
+    // same quad sum, so a mirror adds the same value an xor 4 / xor 8
+    // exchange would: the keys equal those of a shuffle reduction bit for bit)
+    static_assert(LPR == 8 || LPR == 16, "lanes per row");
+    d += dpp_f64<0xB1>(d);  // quad_perm [1,0,3,2]
+    d += dpp_f64<0x4E>(d);  // quad_perm [2,3,0,1]
+    d += dpp_f64<0x141>(d);  // row_half_mirror
+    if constexpr (LPR == 16) d += dpp_f64<0x140>(d);  // row_mirror
     const float pf = (float)(d - muv) + 0.0f;  // + 0 folds -0 into +0
     return ~float_order_key(pf);
   }
