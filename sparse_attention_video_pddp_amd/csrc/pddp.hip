@@ -846,33 +846,41 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D 
   }
   if (tid < D) sY[0][tid] = 1.0f / sqrtf((float)D);
   __syncthreads();
-  // Every lane reads the rows 8g + 4h + 0..3 of each 32-row block of y, and
-  // its partner lane (h ^ 1) the others, so ||y||^2 is an in-lane sum plus
-  // one exchange, formed by every wave alike: no reduction across waves.  The
-  // step's scale 1/||y_k|| uses the hardware reciprocal square root (the
-  // direction does not depend on the scale; v is normalised in fp64 below).
+  // Every lane reads the rows 8g + 4h + 0..3 of each 32-row block of y for
+  // C y.  ||y||^2 is formed by every wave alike, so no reduction across waves
+  // is needed: each lane squares entries l and l + 64, then a sum over the
+  // wave by DPP moves and two lane-half swaps (every lane ends with the same
+  // bits).  The step's scale 1/||y_k|| uses the hardware reciprocal square
+  // root (the direction does not depend on the scale; v is normalised in fp64
+  // below).
   auto read_y = [&](int buf, f32x4 (&yv)[NB][4]) {
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int g = 0; g < 4; ++g) yv[bi][g] = *(const f32x4*)&sY[buf][bi * 32 + 8 * g + 4 * h];
   };
-  auto norm2 = [&](const f32x4 (&yv)[NB][4]) {
-    float q[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = fmaf(yv[bi][g][e], yv[bi][g][e], q[e]);
-    return half_sum((q[0] + q[1]) + (q[2] + q[3]));
+  auto norm2 = [&](int buf) {
+    const float y0 = sY[buf][l];
+    float q = y0 * y0;
+    if constexpr (D > 64) {
+      const float y1 = sY[buf][l + 64];
+      q = fmaf(y1, y1, q);
+    }
+    q += dpp_f32<0xB1>(q);   // quad_perm [1,0,3,2]
+    q += dpp_f32<0x4E>(q);   // quad_perm [2,3,0,1]
+    q += dpp_f32<0x141>(q);  // row_half_mirror
+    q += dpp_f32<0x140>(q);  // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+    q = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);  // rows 0+1, 2+3 of 16 lanes
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
   };
   int cur = 0, last = 0;
   float nl = 1.0f;  // ||y_last||^2
   for (int it = 0; it < p.iters; ++it) {
     f32x4 yv[NB][4];
     read_y(cur, yv);
-    const float nrm2 = norm2(yv);
+    const float nrm2 = norm2(cur);
     if (nrm2 == 0.0f) break;  // C v = 0: keep the previous direction
     last = cur;
     nl = nrm2;
@@ -896,9 +904,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D 
     cur = nxt;
   }
   {
-    f32x4 yv[NB][4];
-    read_y(cur, yv);
-    const float nrm2 = norm2(yv);
+    const float nrm2 = norm2(cur);
     if (nrm2 != 0.0f) {
       last = cur;
       nl = nrm2;
