@@ -402,6 +402,22 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
 // With v_k = y_k / ||y_k||, the iteration runs as y_{k+1} = C y_k / ||y_k||:
 // the norm of y_k is reduced while y_{k+1} is formed, so one barrier per step
 // suffices (y double-buffered in sY).  If C v_k = 0 the direction stays v_k.
+// Sum over the 64 lanes, in every lane: DPP within rows of 16, then the
+// 16-lane and 32-lane half swaps (no LDS permutes).
+__device__ __forceinline__ double wave_sum16_f64(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  // r[0] + r[1]: the even row's value plus the odd row's, in both rows
+  v = __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0])) +
+      __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+  return v + partner32_f64(v);
+}
+
 template <int D, int YB>
 __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* sS, const double* sR, double* sV,
                                      double (*sY)[D], double (*sRed)[4], int n, int iters) {
@@ -437,7 +453,7 @@ __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* s
     const double nrm2 = (sRed[cur][0] + sRed[cur][1]) + (sRed[cur][2] + sRed[cur][3]);
     if (nrm2 == 0.0) break;  // C v = 0: keep the previous direction
     last = cur;
-    const double inv = 1.0 / sqrt(nrm2);
+    const double inv = __builtin_amdgcn_rsq(nrm2);  // any scale serves: the direction is scale-free
     double wv = 0.0;
     if (gw) {
       double part[NB];  // independent FMA chains, one per row block
@@ -459,7 +475,7 @@ __device__ double centre_and_iterate(double (&cacc)[D / 32][16], const double* s
       wv += partner32_f64(wv);
       wv *= inv;
     }
-    const double sq = wave_sum_f64((gw && h == 0) ? wv * wv : 0.0);
+    const double sq = wave_sum16_f64((gw && h == 0) ? wv * wv : 0.0);
     const int nxt = cur ^ 1;
     if (gw && h == 0) sY[nxt][w * 32 + ln] = wv;
     if (l == 0 && w < 4) sRed[nxt][w] = gw ? sq : 0.0;
