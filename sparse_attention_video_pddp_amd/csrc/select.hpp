@@ -36,13 +36,28 @@
 
 namespace mcs {
 
+// Inclusive prefix sum over one 64-lane wave by DPP moves: shifts within each
+// row of 16 lanes (the first three from the original values, then by 4 and 8
+// in the upper banks), then the last lane of row 0 into row 1 and of row 2
+// into row 3, then lane 31 into rows 2 and 3.  No LDS permutes.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
+  int s = x + __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);          // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xF, 0xF, true);          // row_shr:3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xE, true);          // row_shr:4, lanes 4..15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xC, true);          // row_shr:8, lanes 8..15
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);         // row_bcast:15 into rows 1, 3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);         // row_bcast:31 into rows 2, 3
+  return s;
+}
+
 // Exclusive block scan over NT threads; `total` receives the block sum.
 // Two barriers; s_w holds NT/64 ints.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
   constexpr int NW = NT / 64;
   const int w = wave_id();
-  const int x = wave_incl_scan(v);
+  const int x = wave_incl_scan_dpp(v);
   if (lane_id() == 63) s_w[w] = x;
   __syncthreads();
   int off = 0, tot = 0;
