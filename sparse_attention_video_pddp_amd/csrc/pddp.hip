@@ -648,8 +648,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 
 // ---- small nodes ------------------------------------------------------------
 // Nodes of at most kSmallRows rows (the deep levels: thousands of nodes, each a
-// chain of latencies) run with a lighter state so that more workgroups share
-// a CU (three at d = 128, four at d = 64): the scatter sums of the shifted
+// chain of latencies) run with a lighter state so that four workgroups share
+// a CU (at d = 128: 128 registers, with a few spills in the one-time
+// centring, and 39 KB of LDS): the scatter sums of the shifted
 // rows y = x - r (r: the node's first member row; y = hi + lo in two bf16
 // parts, see split_shifted) stay in the fp32 MFMA accumulators over all tiles
 // (exact products, fp32 sums over at most kSmallRows rows), the centring is
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 constexpr int kSmallRows = 512;
 
 template <int D>
-__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3, D == 64 ? 4 : 3))) void pddp_small_kernel(PddpParams p) {
+__global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void pddp_small_kernel(PddpParams p) {
   constexpr int NB = D / 32;
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int RPL = 64 / CH;         // rows per wave-wide copy
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D 
   static_assert(LPW >= 1, "tile copy split");
   using Sel = BlockSelect<kNodeThreads, VPT>;
   // at d = 128 the block select's tables share the ring slots, which are
-  // free once the scatter sums are formed (39 KB of LDS: three workgroups per
+  // free once the scatter sums are formed (39 KB of LDS: four workgroups per
   // CU instead of two)
   constexpr bool kShInSlots = sizeof(typename Sel::Shared) <= 3 * TILE;
   __shared__ __attribute__((aligned(1024))) unsigned char slots[3 * TILE];
@@ -894,8 +895,6 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D 
   int cur = 0, last = 0;
   float nl = 1.0f;  // ||y_last||^2
   for (int it = 0; it < p.iters; ++it) {
-    f32x4 yv[NB][4];
-    read_y(cur, yv);
     const float nrm2 = norm2(cur);
     if (nrm2 == 0.0f) break;  // C v = 0: keep the previous direction
     last = cur;
@@ -903,12 +902,21 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(D 
     const float inv = __builtin_amdgcn_rsqf(nrm2);
     float wv = 0.0f;
     if (gw) {
+      // y read two row blocks at a time (fewer registers: four workgroups per CU)
       float part[NB];
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi) {
-        part[bi] = 0.0f;
+      for (int b0 = 0; b0 < NB; b0 += 2) {
+        f32x4 yv[2][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part[bi] = fmaf(cf[bi][i], yv[bi][i >> 2][i & 3], part[bi]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) yv[j][g] = *(const f32x4*)&sY[cur][(b0 + j) * 32 + 8 * g + 4 * h];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          part[b0 + j] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part[b0 + j] = fmaf(cf[b0 + j][i], yv[j][i >> 2][i & 3], part[b0 + j]);
+        }
       }
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) wv += part[bi];
