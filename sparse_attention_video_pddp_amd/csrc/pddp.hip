@@ -52,7 +52,7 @@ namespace {
 
 constexpr int kNodeThreads = 256;
 constexpr int kSplitThreads = 512;
-constexpr int kSplitWideThreads = 1024;  // nodes of 8193..81920 rows
+constexpr int kSplitWideThreads = 1024;  // nodes of more than 8192 rows
 constexpr int kProjRows = 512;      // rows per workgroup of the projection kernel
 constexpr int kMaxChunkRows = 4096;  // row chunk of the many-workgroup levels; larger nodes split there
 
@@ -253,14 +253,6 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
       for (int i = 1; i < 16; ++i) sv = (si == i) ? accS[i] : sv;
       sacc += (double)sv;
     };
-    // d = 64: wave w < 2 forms both blocks of its column
-    auto compute = [&](const unsigned char* slot) {
-      if (w >= NB) return;
-      f32x16 accS = {};
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi) block(slot, bi, w, bi == 0, accS);
-      add_sums(accS);
-    };
     // d = 128: the matrix is symmetric, so only ten of its sixteen blocks are
     // formed: wave W the blocks (W, W), (W+1, W) and, for W < 2, (W+2, W)
     // (indices mod 4), all in its own column; the blocks of its column formed
@@ -359,7 +351,44 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
         default: run(std::integral_constant<int, 3>{}); break;
       }
     } else {
-      tiles(compute);
+      // d = 64: three of the four blocks, one per wave: (0, 0) by wave 0,
+      // (1, 1) by wave 1, (1, 0) by wave 2, which passes it through the first
+      // tile slot (layout as above) to wave 0 as it is and to wave 1
+      // transposed; wave 3 only copies and splits tiles
+      auto run = [&](auto wc) {
+        constexpr int W = decltype(wc)::value;
+        tiles([&](const unsigned char* slot) {
+          f32x16 accS = {};
+          if constexpr (W < 2) {
+            block(slot, W, W, true, accS);
+            add_sums(accS);
+          } else if constexpr (W == 2) {
+            block(slot, 1, 0, false, accS);
+          }
+        });
+        double* X = (double*)slot0;
+        __syncthreads();  // every operand read of the last tile is done
+        if constexpr (W == 2) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+            X[r * 32 + (ln ^ r)] = cacc[1][i];
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+          if constexpr (W == 0) cacc[1][i] = X[r * 32 + (ln ^ r)];
+          if constexpr (W == 1) cacc[0][i] = X[ln * 32 + (r ^ ln)];
+        }
+      };
+      switch (__builtin_amdgcn_readfirstlane(w)) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        default: run(std::integral_constant<int, 3>{}); break;
+      }
     }
     if (w < NB && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = sacc;
     __syncthreads();
@@ -730,7 +759,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
   // y^T operands from the split tile (hi part in the slot, lo part in slotlo);
   // the blocks (a, c) with a in rows, c in columns, formed for every a in `as`
-  auto compute_blocks = [&](const unsigned char* slot, int c, auto... as) {
+  auto compute_blocks = [&](const unsigned char* slot, int c, bool sums, auto... as) {
 #pragma unroll
     for (int ks2 = 0; ks2 < TR / 16; ++ks2) {
       auto part = [&](const unsigned char* t, int b) {
@@ -746,14 +775,11 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
         acc[bi] = mfma_32x32x16(lb, wl, acc[bi]);
       };
       (one(as), ...);
-      accS = mfma_32x32x16(wh, ones, accS);
-      accS = mfma_32x32x16(wl, ones, accS);
+      if (sums) {
+        accS = mfma_32x32x16(wh, ones, accS);
+        accS = mfma_32x32x16(wl, ones, accS);
+      }
     }
-  };
-  // d = 64: wave w < 2 forms both blocks of its column
-  auto compute = [&](const unsigned char* slot) {
-    if (!gw) return;
-    compute_blocks(slot, w, 0, 1);
   };
   // Tile t lands in slot t % 3 by copies issued two tiles ahead (ids loaded a
   // tile before their copies); after a barrier it is split in place (low
@@ -798,8 +824,8 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
     auto xblk = [&](int m) { return (float*)(m < 4 ? ring[m >> 1] + (m & 1) * 4096 : slotlo + (m - 4) * 4096); };
     auto run = [&](auto wc) {
       constexpr int W = decltype(wc)::value;
-      if constexpr (W < 2) tiles([&](const unsigned char* slot) { compute_blocks(slot, W, W, (W + 1) & 3, W + 2); });
-      else tiles([&](const unsigned char* slot) { compute_blocks(slot, W, W, (W + 1) & 3); });
+      if constexpr (W < 2) tiles([&](const unsigned char* slot) { compute_blocks(slot, W, true, W, (W + 1) & 3, W + 2); });
+      else tiles([&](const unsigned char* slot) { compute_blocks(slot, W, true, W, (W + 1) & 3); });
       __syncthreads();  // every operand read of the last tile is done
       auto put = [&](int m, int a) {
         float* X = xblk(m);
@@ -838,7 +864,37 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       default: run(std::integral_constant<int, 3>{}); break;
     }
   } else {
-    tiles(compute);
+    // d = 64: (0, 0) by wave 0, (1, 1) by wave 1, (1, 0) by wave 2, passed
+    // through the first slot to wave 0 as it is and to wave 1 transposed
+    auto run = [&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      tiles([&](const unsigned char* slot) {
+        if constexpr (W < 2) compute_blocks(slot, W, true, W);
+        else if constexpr (W == 2) compute_blocks(slot, 0, false, 1);
+      });
+      float* X = (float*)slot0;
+      __syncthreads();  // every operand read of the last tile is done
+      if constexpr (W == 2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+          X[r * 32 + (ln ^ r)] = acc[1][i];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        if constexpr (W == 0) acc[1][i] = X[r * 32 + (ln ^ r)];
+        if constexpr (W == 1) acc[0][i] = X[ln * 32 + (r ^ ln)];
+      }
+    };
+    switch (wu) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      default: run(std::integral_constant<int, 3>{}); break;
+    }
   }
   // column sums: lane (n, h) of wave w keeps element n%16: S[32w + 8((n%16)/4) + 4h + n%4]
   {
@@ -1179,17 +1235,29 @@ struct Plan {
   size_t part, red, vec;  // doubles
 };
 
-// Rows per partial scatter sum at a many-workgroup level: as many chunks per
-// node as keep the level's chunks within one round of two gram workgroups
-// per CU (512 on 256 CUs), at least 512 rows each.  (A fixed chunk of
-// BH*Nq/512 rows gave every level a few more than 512 chunks, so each gram
-// launch ran a second, almost empty round: twice its time.)
+// Rows per partial scatter sum at a many-workgroup level (a multiple of 64,
+// at least 512): the chunking whose rounds of two gram workgroups per CU
+// (512 on 256 CUs) take the fewest tile times, each chunk's partial sums
+// counted as 1/200 of a tile time (they are written and reduced).  (A fixed
+// chunk of BH*Nq/512 rows gave every level a few more than 512 chunks, so
+// each gram launch ran a second, almost empty round: twice its time; at 40
+// heads one chunk per node left 320 long workgroups on 512 slots.)
 constexpr int kGramSlots = 512;
 long long gram_chunk_rows(long long maxn, int BH, int nslots) {
-  const long long per_node = std::max(1LL, (long long)kGramSlots / ((long long)BH * nslots));
-  long long cg = (maxn + per_node - 1) / per_node;
-  cg = (cg + 63) / 64 * 64;
-  return cg < 512 ? 512 : cg;
+  const long long nodes = (long long)BH * nslots, tiles = (maxn + 63) / 64;
+  long long best_rows = tiles * 64, best_cost = -1;
+  for (long long c = 1; c <= tiles; ++c) {
+    const long long rows = ((maxn + c - 1) / c + 63) / 64 * 64;
+    if (rows < 512 && c > 1) break;
+    const long long chunks = nodes * ((maxn + rows - 1) / rows);
+    const long long rounds = (chunks + kGramSlots - 1) / kGramSlots;
+    const long long cost = 200 * rounds * (rows / 64) + chunks;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_rows = rows;
+    }
+  }
+  return best_rows;
 }
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
@@ -1256,7 +1324,8 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
         hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 80>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
                            st, p);
       else
-        hipLaunchKernelGGL((pddp_split_kernel<kSplitThreads, 0>), dim3(nslots, s.BH), dim3(kSplitThreads), 0, st, p);
+        hipLaunchKernelGGL((pddp_split_kernel<kSplitWideThreads, 0>), dim3(nslots, s.BH), dim3(kSplitWideThreads), 0,
+                           st, p);
     } else {
       const dim3 grid(nslots, s.BH);
       static_assert(kMaxChunkRows <= 16 * kNodeThreads, "node kernel register cache");
