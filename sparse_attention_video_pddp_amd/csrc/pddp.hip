@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 // (exact products, fp32 sums over at most kSmallRows rows), the centring is
 // done in fp64 and the power iteration runs in fp32 (C rounded to fp32); the
 // projections stay fp64.  Row tiles of 32 rows in a three-slot ring.
-constexpr int kSmallRows = 512;
+constexpr int kSmallRows = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void pddp_small_kernel(PddpParams p) {
@@ -712,7 +712,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
   __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D], sR[D], sV[D], sMu[4];
   __shared__ __attribute__((aligned(16))) float sY[2][D];
-  __shared__ uint32_t s_keys[kSmallRows];
+  // the projection keys in the low-part slot, free once the scatter is formed
+  static_assert(kSmallRows * 4 <= TILE, "keys in the low-part slot");
+  uint32_t* const s_keys = (uint32_t*)slotlo;
   const int bh = blockIdx.y;
   const Node nd = pddp_node(blockIdx.x, p.level, p.Nq, p.G);
   if (nd.c <= 1) return;
