@@ -23,23 +23,25 @@
 //      stay in ascending token order, so position order is index order).
 //
 // Two schedules.  Levels whose nodes are larger than `cr` rows (the top of
-// the tree, few nodes) are spread over many workgroups: row chunks of cr
-// rows produce partial sums (step 1), an ordered reduction adds them, one
-// workgroup per node iterates (step 2), row chunks project (step 3) and one
-// workgroup per node splits (step 4, select.hpp).  Smaller nodes are done by
-// one workgroup each from start to end, with the projection keys and member
-// ids kept in registers.
+// the tree, few nodes) are spread over many workgroups: row chunks produce
+// partial sums (step 1), an ordered reduction adds them, one workgroup per
+// node iterates (step 2), row chunks project (step 3) and one workgroup per
+// node splits (step 4, select.hpp).  Smaller nodes are done by one workgroup
+// each from start to end, with the projection keys and member ids kept on
+// chip (pddp_node_kernel, and pddp_small_kernel for nodes of at most 1024
+// bf16 rows).
 //
-// In step 1 the gathered rows of a 64-row tile are copied straight into LDS
-// (global_load_lds, 16 bytes per lane) in a ring of two slots (one workgroup
-// per node) or three (row chunks of the many-workgroup levels, and the
-// small-node kernel's 32-row tiles), row-major with the 16-byte chunks
-// XOR-swizzled per row; both MFMA operands (x^T blocks) are read with
-// ds_read_b64_tr_b16.  The partial sums of the many-workgroup levels cover
-// chunks of cg rows, set per level so that a level has at most 512 chunks over
-// all heads (one round of two workgroups per CU).  Wave w holds column block w of the scatter
-// matrix in the MFMA output layout (lane: one column, 16 rows per 32-row
-// block), so C v needs only an in-lane sum and one half-wave exchange.
+// In step 1 the gathered rows of a tile (64 rows; 32 in the small-node
+// kernel) are copied straight into LDS (global_load_lds, 16 bytes per lane)
+// in a ring of two slots (pddp_node_kernel) or three, row-major with the
+// 16-byte chunks XOR-swizzled per row; both MFMA operands (x^T blocks) are
+// read with ds_read_b64_tr_b16.  The scatter matrix is symmetric, so only
+// the blocks of one triangle are formed (ten of sixteen 32x32 blocks at
+// d = 128, three of four at d = 64), spread over the waves; the chunks of
+// the many-workgroup levels are sized per level (gram_chunk_rows).  For the
+// power iteration wave w holds column block w of C in the MFMA output layout
+// (lane: one column, 16 rows per 32-row block), so C v needs only an in-lane
+// sum and one half-wave exchange.
 #include <algorithm>
 #include <type_traits>
 
