@@ -375,6 +375,17 @@ def reuse_flops(w) -> float:
     return 4.0 * w.d * w.Nq * w.k * w.B * w.H
 
 
+def workload_kind(w) -> str:
+    """The attention pattern and sizes of a workload, in words."""
+    t, y, x = w.grid
+    gen = "Fourier-feature Q/K" if w.generator == "fourier" else "smoothed-random-field Q/K"
+    if w.causal_block and w.q_frames is not None:
+        t0, t1 = w.q_frames
+        return (f"frame-block-causal attention of a {t1 - t0}-frame query chunk (frames {t0}..{t1 - 1}, "
+                f"{w.Nq} tokens) over a {t}x{y}x{x} = {w.Nkv}-token K/V cache, {gen}")
+    return f"full bidirectional 3D attention over a {t}x{y}x{x} = {w.Nkv}-token video latent, {gen}"
+
+
 def cpu_baseline(w, host0, host1, nheads: int, reuse_budget_s: float = 10.0):
     """The oracle as it stands, on a bounded sample: its own anchor (PDDP,
     dense attention, column mass, top-k, residual) prepares each sampled
@@ -804,12 +815,11 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: full bidirectional 3D attention over a {w.grid[0]}x{w.grid[1]}x"
-                               f"{w.grid[2]} = {w.Nkv}-token video latent, B={w.B}, H={w.H}, d={w.d}, "
+        "config": {"workload": f"{w.name}: {workload_kind(w)}, B={w.B}, H={w.H}, d={w.d}, "
                                f"{w.dtype}, PDDP groups of {w.group_size}, keep {w.keep_permille / 10:g}% "
                                f"(k={w.k}), anchor every {A} steps, drift {w.drift} N(0,1) per step, "
                                f"residual R in float32",
-                   "B": w.B, "H": w.H, "N": w.Nkv, "d": w.d, "group_size": w.group_size, "k": w.k,
+                   "B": w.B, "H": w.H, "N": w.Nkv, "Nq": w.Nq, "d": w.d, "group_size": w.group_size, "k": w.k,
                    "anchor_every": A, "residual": "float32"},
         "step": f"one anchor period: mcs_group + mcs_anchor on step 0, mcs_sparse_attn on steps 1..{A - 1}",
         "value_is": "executed TFLOP/s of the reuse step (mcs_sparse_attn): 4*Nq*k*d*H FLOPs per call over the "
