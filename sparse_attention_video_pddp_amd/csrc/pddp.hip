@@ -7,15 +7,19 @@
 // the node's shape (start, n, c groups) follows from its slot number alone.
 // For a node with c >= 2 groups:
 //   1. S = sum y and the scatter sum y y^T over the node's rows, where
-//      y = x - r is the row shifted by the node's first member row r (bf16
-//      inputs; fp32 inputs use r = 0): bf16 rows go through
+//      y = x - r is the row shifted by a bf16 row r (bf16 inputs; fp32 inputs
+//      use r = 0): the head's row 0 at the many-workgroup levels, the node's
+//      first member row in pddp_node_kernel, the parent's mean row rounded
+//      to bf16 in pddp_small_kernel; bf16 rows go through
 //      v_mfma_f32_32x32x16_bf16 as y = hi + lo, two bf16 parts (exact
 //      products, fp32 sums over 64-row tiles, fp64 across tiles), fp32 rows
 //      with fp64 FMAs.  Without the shift, queries sharing a large mean would
 //      make sum x x^T and S S^T / n nearly equal, and their fp32 sums would
 //      lose the spread around the mean that the direction is taken from;
 //   2. C = sum y y^T - S S^T / n (fp64, the same matrix as for x since
-//      centring removes any shift) and the fixed-step power iteration
+//      centring removes any shift; below the root the many-workgroup levels
+//      form the sums of left children only and take a right child's as its
+//      parent's minus its sibling's) and the fixed-step power iteration
 //      v <- C v / ||C v|| from v0 = 1/sqrt(d) in fp64 (a zero product keeps v);
 //   3. projections p_i = x_i . v - (r + S/n) . v in fp64, keyed by float(p_i);
 //   4. the floor(c/2)*G members of smallest key, equal keys lowest position
@@ -64,7 +68,10 @@ struct PddpParams {
   int32_t* tmp;
   uint32_t* keys;
   double* part;  // [BH][nslots][pmax][D + D*D] partial (S, sum x x^T) per row chunk
-  double* red;   // [BH][nslots][D + D*D] their sums
+  double* red;       // [BH][nslots][D + D*D] their sums at this level
+  double* red_prev;  // the same at the level above (many-workgroup levels below the root)
+  __bf16* mean_cur;          // [BH][nslots][D] each node's mean row rounded to bf16 (bf16 inputs)
+  const __bf16* mean_prev;   // the same at the level above: the small-node kernel's shift
   double* vec;   // [BH][nslots][D + 1] direction v and (S/n) . v
   int Nq, G, iters, level, cr, pmax;
   int cg;       // rows per partial scatter sum (a chunk of a node) at the many-workgroup levels
@@ -119,6 +126,16 @@ __device__ __forceinline__ void split_tile(unsigned char* slot, unsigned char* l
   }
 }
 
+// Row `tid` < D of a node's mean, r + S/n (S: the sums of the rows shifted
+// by r), rounded to bf16: the children's shift in the small-node kernel.
+template <int D>
+__device__ __forceinline__ void store_mean(const PddpParams& p, int bh, int slot, const double* sR, const double* sS,
+                                           int n) {
+  const int tid = threadIdx.x;
+  if (tid < D)
+    p.mean_cur[(((size_t)bh << p.level) + slot) * D + tid] = (__bf16)(sR[tid] + sS[tid] / (double)n);
+}
+
 // Shape of node `slot` of `level` (c == 0: the slot lies under a leaf).
 __device__ __forceinline__ Node pddp_node(int slot, int level, int Nq, int G) {
   Node nd{0, Nq, (Nq + G - 1) / G};
@@ -158,8 +175,9 @@ struct GramLds {
 // Step 1 over member rows [r0, r1) of a node (nperm: the node's members).
 // cacc (waves w < NB): sum y y^T, element (bi, i) = row 32*bi + 8*(i/4) +
 // 4*h + i%4, column 32*w + lane%32.  sS[0..D): sum y.  For bf16 rows
-// y = x - Q[nperm[0]] (the node's first member row), for fp32 rows y = x.
-// Ends with a barrier.
+// y = x - Q[shift] (a row of the head: the node's first member row in the
+// node kernel, the head's row 0 at the many-workgroup levels), for fp32 rows
+// y = x.  Ends with a barrier.
 // Partial sums of the many-workgroup levels: S (D doubles), then the
 // scatter matrix.  bf16 rows at d = 128 form only the ten blocks of one
 // triangle (gram_rows), stored as ten 32x32 blocks in the MFMA output layout
@@ -172,7 +190,7 @@ template <int D, bool BF16>
 constexpr int kPartE = kSymPart<D, BF16> ? D + 10 * 1024 : D + D * D;
 
 template <int D, bool BF16, int NS, bool XCH = true>
-__device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1,
+__device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, int r0, int r1, int shift,
                           unsigned char* slot0, unsigned char* slot1, unsigned char* slot2, unsigned char* slotlo,
                           float* sRf, double (&cacc)[D / 32][16], double* sS) {
   using C = GramCfg<D>;
@@ -194,9 +212,9 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
     const int ob1 = (8 + vr) * (2 * D) + 8 * (l & 1) + 16 * (c0 ^ swz<D>(8 + vr));
     const int lrow0 = l / C::CH, lchunk = l % C::CH;
     const int ntiles = (r1 - r0 + 63) / 64;
-    // the shift r: the node's first member row, in LDS as float32 (published by
+    // the shift r: row `shift` of the head, in LDS as float32 (published by
     // the first barrier of the tile loop)
-    if (tid < D) sRf[tid] = (float)Qh[(size_t)nperm[0] * D + tid];
+    if (tid < D) sRf[tid] = (float)Qh[(size_t)shift * D + tid];
     // column sums: lane (n, h) of wave w keeps element n%16 of the ones-product,
     // i.e. S[32w + 8((n%16)/4) + 4h + n%4]
     double sacc = 0.0;
@@ -208,7 +226,7 @@ __device__ void gram_rows(const void* Qv, size_t hbase, const int32_t* nperm, in
       for (int j = 0; j < C::LPW; ++j) {
         const int r = C::RPL * (w + 4 * j) + lrow0;
         const int i = r0 + t * 64 + r;
-        ids[j] = nperm[i < r1 ? i : 0];  // tail rows: the shift row, which shifts to exactly 0
+        ids[j] = i < r1 ? nperm[i] : shift;  // tail rows: the shift row, which shifts to exactly 0
       }
     };
     auto issue = [&](unsigned char* slot) {
@@ -657,7 +675,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   int32_t* nperm = p.perm + hbase + nd.start;
   if (BF16 && (int)threadIdx.x < D) sR[threadIdx.x] = (double)(float)((const __bf16*)p.Q)[(hbase + nperm[0]) * D + threadIdx.x];
   double cacc[D / 32][16];
-  gram_rows<D, BF16, 2>(p.Q, hbase, nperm, 0, nd.n, slot0, slot1, slot1, slotlo, sRf, cacc, sS);  // its final barrier publishes sR
+  gram_rows<D, BF16, 2>(p.Q, hbase, nperm, 0, nd.n, nperm[0], slot0, slot1, slot1, slotlo, sRf, cacc,
+                        sS);  // its final barrier publishes sR
+  if constexpr (BF16) store_mean<D>(p, bh, blockIdx.x, sR, sS, nd.n);
   const double muv = centre_and_iterate<D, D / 64>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
   project_rows<D, BF16, kNodeThreads>(p.Q, hbase, nperm, 0, nd.n, sV, muv, [&](int i, uint32_t k) { s_keys[i] = k; });
   __syncthreads();
@@ -682,8 +702,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 // chain of latencies) run with a lighter state so that four workgroups share
 // a CU (at d = 128: 128 registers, with a few spills in the one-time
 // centring, and 39 KB of LDS): the scatter sums of the shifted
-// rows y = x - r (r: the node's first member row; y = hi + lo in two bf16
-// parts, see split_shifted) stay in the fp32 MFMA accumulators over all tiles
+// rows y = x - r (r: the parent's mean row rounded to bf16, the first member
+// row at the root; y = hi + lo in two bf16 parts, see split_shifted) stay in
+// the fp32 MFMA accumulators over all tiles
 // (exact products, fp32 sums over at most kSmallRows rows), the centring is
 // done in fp64 and the power iteration runs in fp32 (C rounded to fp32); the
 // projections stay fp64.  Row tiles of 32 rows in a three-slot ring.
@@ -729,7 +750,14 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
 
   // ---- 1. scatter sums of the shifted rows, fp32 over all tiles ---------------
   const __bf16* Qh = (const __bf16*)p.Q + hbase * D;
-  const __bf16* rrow = Qh + (size_t)nperm[0] * D;  // the shift r (published by the tile loop's first barrier)
+  // the shift r: the parent's mean row (bf16) below the root, else the first
+  // member row; published by the tile loop's first barrier.  (With the first
+  // member row the column-mean part of the sums dwarfs the scatter and the
+  // fp32 sums over the tiles moved the projections by up to four times the
+  // parity band on a few nodes in a hundred; shifted by the parent's mean
+  // they stay within a fraction of it.)
+  const __bf16* rrow =
+      p.level > 0 ? p.mean_prev + (((size_t)bh << (p.level - 1)) + (blockIdx.x >> 1)) * D : Qh + (size_t)nperm[0] * D;
   if (tid < D) {
     sR[tid] = (double)(float)rrow[tid];
     sRf[tid] = (float)rrow[tid];
@@ -745,14 +773,14 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int i = t * TR + RPL * (wu + 4 * j) + lrow0;
-      ids[j] = nperm[i < n ? i : 0];  // tail rows: the shift row, which shifts to exactly 0
+      ids[j] = i < n ? nperm[i] : -1;  // tail rows: the shift itself, which shifts to exactly 0
     }
   };
   auto issue = [&](unsigned char* slot) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int r = RPL * (wu + 4 * j) + lrow0;
-      dma16(Qh + (size_t)ids[j] * D + ((lchunk ^ swz<D>(r)) * 8), slot + (wu + 4 * j) * 1024);
+      dma16((ids[j] >= 0 ? Qh + (size_t)ids[j] * D : rrow) + ((lchunk ^ swz<D>(r)) * 8), slot + (wu + 4 * j) * 1024);
     }
   };
   bf16x8 ones;
@@ -909,6 +937,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
     if (gw && ln < 16) sS[32 * w + 8 * (si >> 2) + 4 * h + (si & 3)] = (double)sv;
   }
   __syncthreads();
+  store_mean<D>(p, bh, blockIdx.x, sR, sS, n);
 
   // ---- 2. centre in fp64, iterate in fp32 ------------------------------------
   const double inv_n = 1.0 / (double)n;
@@ -1031,17 +1060,22 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   __shared__ __attribute__((aligned(1024))) unsigned char slotlo[L::SLOTLO];
   __shared__ __attribute__((aligned(16))) float sRf[D];
   __shared__ double sS[D];
-  const int bh = blockIdx.y, slot = blockIdx.x / p.pmax, chunk = blockIdx.x % p.pmax;
+  // below the root only left children (even slots) are summed: a right
+  // child's sums are its parent's minus its sibling's (pddp_reduce_kernel);
+  // every node of these levels is shifted by the head's row 0, so that the
+  // sums of parent and children share the shift
+  const int below = p.level > 0;
+  const int bh = blockIdx.y, slot = (blockIdx.x / p.pmax) << below, chunk = blockIdx.x % p.pmax;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
-  if (nd.c <= 1) return;
+  if (nd.c <= 1 - below) return;  // the root: split only if c > 1; a left child: needed whenever it exists
   const int r0 = chunk * p.cg;
   if (r0 >= nd.n) return;
   const int r1 = min(nd.n, r0 + p.cg);
   const size_t hbase = (size_t)bh * p.Nq;
   double cacc[D / 32][16];
   constexpr int E = kPartE<D, BF16>;
-  gram_rows<D, BF16, 3, !kSymPart<D, BF16>>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, slot0, slot1, slot2, slotlo,
-                                            sRf, cacc, sS);
+  gram_rows<D, BF16, 3, !kSymPart<D, BF16>>(p.Q, hbase, p.perm + hbase + nd.start, r0, r1, 0, slot0, slot1, slot2,
+                                            slotlo, sRf, cacc, sS);
   const int nslots = 1 << p.level;
   double* out = p.part + (((size_t)bh * nslots + slot) * p.pmax + chunk) * E;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
@@ -1067,7 +1101,9 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-// Ordered sum of a node's partials (same order on every run).
+// Ordered sum of a node's partials (same order on every run).  Below the
+// root a left child's sums are its partials' sum and a right child's are
+// its parent's sums minus that same sum (one fp64 rounding).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   constexpr int E = kPartE<D, BF16>;
@@ -1076,9 +1112,11 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   const int e = (blockIdx.x % RB) * 256 + threadIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
   if (nd.c <= 1 || e >= E) return;
-  const int parts = (nd.n + p.cg - 1) / p.cg;
+  const int left = p.level > 0 ? slot & ~1 : slot;  // the node whose partials were formed
+  const Node nl = left == slot ? nd : pddp_node(left, p.level, p.Nq, p.G);
+  const int parts = (nl.n + p.cg - 1) / p.cg;
   const size_t node = (size_t)bh * (1 << p.level) + slot;
-  const double* src = p.part + node * p.pmax * E + e;
+  const double* src = p.part + ((size_t)bh * (1 << p.level) + left) * p.pmax * E + e;
   // four partials loaded before they are added (four loads in flight), added in chunk order
   double s = 0.0;
   int q = 0;
@@ -1090,6 +1128,7 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
     for (int i = 0; i < 4; ++i) s += v[i];
   }
   for (; q < parts; ++q) s += src[(size_t)q * E];
+  if (left != slot) s = p.red_prev[((size_t)bh * (1 << (p.level - 1)) + (slot >> 1)) * E + e] - s;
   p.red[node * E + e] = s;
 }
 
@@ -1107,9 +1146,10 @@ __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
   double cacc[D / 32][16];
   if (tid < D) sS[tid] = red[tid];
-  // the shift of the partial sums: the node's first member row (bf16 inputs)
+  // the shift of the partial sums: the head's row 0 (bf16 inputs)
   const size_t hbase = (size_t)bh * p.Nq;
-  if (BF16 && tid < D) sR[tid] = (double)(float)((const __bf16*)p.Q)[(hbase + p.perm[hbase + nd.start]) * D + tid];
+  if (BF16 && tid < D) sR[tid] = (double)(float)((const __bf16*)p.Q)[hbase * D + tid];
+  if constexpr (BF16) store_mean<D>(p, bh, slot, sR, sS, nd.n);  // each thread its own entries
   if constexpr (kSymPart<D, BF16>) {
     // block (bi, W) of column W: stored as it is, or as the transpose of the
     // stored block (W, bi); element (r, c) of a stored block sits at
@@ -1237,6 +1277,7 @@ __global__ void pddp_init_kernel(int32_t* perm, int Nq, size_t total) {
 struct Plan {
   int levels, cr;
   size_t part, red, vec;  // doubles
+  size_t mean;            // bf16 values per level of node means
 };
 
 // Rows per partial scatter sum at a many-workgroup level (a multiple of 64,
@@ -1266,6 +1307,10 @@ long long gram_chunk_rows(long long maxn, int BH, int nslots) {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Nodes per head whose scatter is summed at a many-workgroup level: the root,
+// then the left child of each node (the right child's sums are derived).
+int gram_nodes(int level) { return level > 0 ? 1 << (level - 1) : 1; }
+
 long long level_max_rows(const Shape& s, int level) {
   const long long cmax = ((long long)s.c + (1LL << level) - 1) >> level;
   const long long n = cmax * s.G;
@@ -1273,8 +1318,9 @@ long long level_max_rows(const Shape& s, int level) {
 }
 
 Plan make_plan(const Shape& s) {
-  Plan pl{0, 0, 0, 0, 0};
+  Plan pl{0, 0, 0, 0, 0, 0};
   while ((1 << pl.levels) < s.c) ++pl.levels;
+  pl.mean = ((size_t)s.BH << (pl.levels > 0 ? pl.levels - 1 : 0)) * (size_t)s.d;
   long long cr = ((long long)s.BH * s.Nq + 511) / 512;
   cr = (cr + 63) / 64 * 64;
   pl.cr = (int)(cr < 2048 ? 2048 : (cr > kMaxChunkRows ? kMaxChunkRows : cr));
@@ -1283,7 +1329,7 @@ Plan make_plan(const Shape& s) {
     const long long maxn = level_max_rows(s, lv);
     if (maxn <= pl.cr) break;
     const size_t nodes = (size_t)s.BH << lv;
-    const long long cg = gram_chunk_rows(maxn, s.BH, 1 << lv);
+    const long long cg = gram_chunk_rows(maxn, s.BH, gram_nodes(lv));
     const size_t pmax = (size_t)((maxn + cg - 1) / cg);
     pl.part = std::max(pl.part, nodes * pmax * E);
     pl.red = std::max(pl.red, nodes * E);
@@ -1295,14 +1341,20 @@ Plan make_plan(const Shape& s) {
 template <int D, bool BF16>
 void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st) {
   constexpr int RB = (kPartE<D, BF16> + 255) / 256;
+  double* const red[2] = {p.red, p.red + pl.red};  // the level's sums and the level above's
+  __bf16* const mean[2] = {p.mean_cur, p.mean_cur + pl.mean};
   for (int lv = 0; lv < pl.levels; ++lv) {
     p.level = lv;
+    p.mean_cur = mean[lv & 1];
+    p.mean_prev = mean[(lv + 1) & 1];
     const int nslots = 1 << lv;
     const long long maxn = level_max_rows(s, lv);
     if (maxn > pl.cr) {
-      p.cg = (int)gram_chunk_rows(maxn, s.BH, nslots);
+      p.cg = (int)gram_chunk_rows(maxn, s.BH, gram_nodes(lv));
       p.pmax = (int)((maxn + p.cg - 1) / p.cg);
-      const dim3 chunks(nslots * p.pmax, s.BH);
+      p.red = red[lv & 1];
+      p.red_prev = red[(lv + 1) & 1];
+      const dim3 chunks(gram_nodes(lv) * p.pmax, s.BH);
       hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
       hipLaunchKernelGGL((pddp_reduce_kernel<D, BF16>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
       hipLaunchKernelGGL((pddp_power_kernel<D, BF16>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
@@ -1352,7 +1404,8 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
 size_t pddp_workspace_bytes(const Shape& s) {
   const Plan pl = make_plan(s);
   const size_t n = (size_t)s.BH * s.Nq;
-  return 2 * round256(n * 4) + round256(pl.part * 8) + round256(pl.red * 8) + round256(pl.vec * 8);
+  return 2 * round256(n * 4) + round256(pl.part * 8) + round256(2 * pl.red * 8) + round256(pl.vec * 8) +
+         round256(2 * pl.mean * 2);
 }
 
 hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, void* ws, hipStream_t st) {
@@ -1369,8 +1422,10 @@ hipError_t launch_pddp(const Shape& s, bool bf16, const void* Q, int32_t* perm, 
   p.part = (double*)w;
   w += round256(pl.part * 8);
   p.red = (double*)w;
-  w += round256(pl.red * 8);
+  w += round256(2 * pl.red * 8);
   p.vec = (double*)w;
+  w += round256(pl.vec * 8);
+  p.mean_cur = (__bf16*)w;
   p.Nq = s.Nq;
   p.G = s.G;
   p.iters = s.iters;

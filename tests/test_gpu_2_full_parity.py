@@ -43,3 +43,33 @@ def test_full_size_sampled_parity(name):
         for r in reps:
             log(f"  {name} head {bh} groups {groups}: {r}")
         assert_reports(reps, f"{name} head {bh}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["bidir5", "causal", "large", "stress"])
+def test_full_size_groups_every_head(name):
+    """mcs_group at the full size, every head: each split recomputed by the
+    oracle from the GPU's parent set (check_groups_nodewise); the many-
+    workgroup levels derive a right child's sums from its parent's and its
+    sibling's, so every head's top levels are covered here."""
+    import torch
+    from sparse_attention_video_pddp_amd import mcs
+    from sparse_attention_video_pddp_amd.workload import device_inputs
+    from tests.gpu_runner import log
+    from tests.parity import check_groups_nodewise
+    assert torch.cuda.is_available()
+    w = synth.get(name)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    p = mcs.problem_for(w)
+    (Q, K, V), host = device_inputs(w, 0, keep_heads=heads)
+    del K, V
+    perm = torch.empty((w.B, w.H, w.Nq), dtype=torch.int32, device=Q.device)
+    g, _ = mcs.workspace_size(p, mcs.MCS_WS_GROUP)
+    ws = torch.empty(max(g, 1), dtype=torch.uint8, device=Q.device)
+    mcs.group(p, Q, perm, ws)
+    torch.cuda.synchronize()
+    perm_h = perm.cpu().numpy()
+    for (b, h) in heads:
+        rep = check_groups_nodewise(host[(b, h)][0].astype(np.float64), perm_h[b, h], w.group_size, w.pddp_iters)
+        log(f"  {name} head {(b, h)}: {rep}")
+        assert rep.ok, f"{name} head {(b, h)}: {rep}"
