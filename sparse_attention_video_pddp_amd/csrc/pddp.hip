@@ -1102,21 +1102,20 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
 }
 
 // Ordered sum of a node's partials (same order on every run).  Below the
-// root a left child's sums are its partials' sum and a right child's are
-// its parent's sums minus that same sum (one fp64 rounding).
+// root the workgroups of a left child also form its sibling's sums: its
+// parent's sums minus the left child's (one fp64 rounding).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   constexpr int E = kPartE<D, BF16>;
   constexpr int RB = (E + 255) / 256;
-  const int bh = blockIdx.y, slot = blockIdx.x / RB;
+  const int below = p.level > 0;
+  const int bh = blockIdx.y, slot = (blockIdx.x / RB) << below;  // the node whose partials were formed
   const int e = (blockIdx.x % RB) * 256 + threadIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
-  if (nd.c <= 1 || e >= E) return;
-  const int left = p.level > 0 ? slot & ~1 : slot;  // the node whose partials were formed
-  const Node nl = left == slot ? nd : pddp_node(left, p.level, p.Nq, p.G);
-  const int parts = (nl.n + p.cg - 1) / p.cg;
+  if (nd.c <= 1 - below || e >= E) return;
+  const int parts = (nd.n + p.cg - 1) / p.cg;
   const size_t node = (size_t)bh * (1 << p.level) + slot;
-  const double* src = p.part + ((size_t)bh * (1 << p.level) + left) * p.pmax * E + e;
+  const double* src = p.part + node * p.pmax * E + e;
   // four partials loaded before they are added (four loads in flight), added in chunk order
   double s = 0.0;
   int q = 0;
@@ -1128,8 +1127,8 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
     for (int i = 0; i < 4; ++i) s += v[i];
   }
   for (; q < parts; ++q) s += src[(size_t)q * E];
-  if (left != slot) s = p.red_prev[((size_t)bh * (1 << (p.level - 1)) + (slot >> 1)) * E + e] - s;
   p.red[node * E + e] = s;
+  if (below) p.red[(node + 1) * E + e] = p.red_prev[((size_t)bh * (1 << (p.level - 1)) + (slot >> 1)) * E + e] - s;
 }
 
 template <int D, bool BF16>
@@ -1356,7 +1355,7 @@ void launch_levels(const Shape& s, const Plan& pl, PddpParams p, hipStream_t st)
       p.red_prev = red[(lv + 1) & 1];
       const dim3 chunks(gram_nodes(lv) * p.pmax, s.BH);
       hipLaunchKernelGGL((pddp_gram_kernel<D, BF16>), chunks, dim3(kNodeThreads), 0, st, p);
-      hipLaunchKernelGGL((pddp_reduce_kernel<D, BF16>), dim3(nslots * RB, s.BH), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((pddp_reduce_kernel<D, BF16>), dim3(gram_nodes(lv) * RB, s.BH), dim3(256), 0, st, p);
       hipLaunchKernelGGL((pddp_power_kernel<D, BF16>), dim3(nslots, s.BH), dim3(kNodeThreads), 0, st, p);
       p.pj_pmax = (int)((maxn + kProjRows - 1) / kProjRows);
       hipLaunchKernelGGL((pddp_project_kernel<D, BF16>), dim3(nslots * p.pj_pmax, s.BH), dim3(256), 0, st, p);
