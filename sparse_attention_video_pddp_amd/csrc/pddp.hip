@@ -1322,7 +1322,7 @@ Plan make_plan(const Shape& s) {
   pl.mean = ((size_t)s.BH << (pl.levels > 0 ? pl.levels - 1 : 0)) * (size_t)s.d;
   long long cr = ((long long)s.BH * s.Nq + 511) / 512;
   cr = (cr + 63) / 64 * 64;
-  pl.cr = (int)(cr < 2048 ? 2048 : (cr > kMaxChunkRows ? kMaxChunkRows : cr));
+  pl.cr = (int)(cr < 1024 ? 1024 : (cr > kMaxChunkRows ? kMaxChunkRows : cr));
   const size_t E = (size_t)s.d + (size_t)s.d * s.d;
   for (int lv = 0; lv < pl.levels; ++lv) {
     const long long maxn = level_max_rows(s, lv);
