@@ -51,7 +51,8 @@ def test_full_size_groups_every_head(name):
     """mcs_group at the full size, every head: each split recomputed by the
     oracle from the GPU's parent set (check_groups_nodewise); the many-
     workgroup levels derive a right child's sums from its parent's and its
-    sibling's, so every head's top levels are covered here."""
+    sibling's, so every head's top levels are covered here.  (bidir10's
+    queries are bidir5's: the keep fraction does not enter the grouping.)"""
     import torch
     from sparse_attention_video_pddp_amd import mcs
     from sparse_attention_video_pddp_amd.workload import device_inputs
