@@ -697,6 +697,86 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(2,
   });
 }
 
+// The fixed-step power iteration in fp32 on C held in the MFMA output layout
+// (cf, waves w < D/32: column block w), from v0 = 1/sqrt(d); the direction,
+// normalised in fp64, goes to sV.  Ends with a barrier.
+template <int D>
+__device__ __forceinline__ void power_f32(const float (&cf)[D / 32][16], float (*sY)[D], double* sV, int iters) {
+  constexpr int NB = D / 32;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), ln = l & 31, h = l >> 5;
+  const bool gw = w < NB;
+  if (tid < D) sY[0][tid] = 1.0f / sqrtf((float)D);
+  __syncthreads();
+  // Every lane reads the rows 8g + 4h + 0..3 of each 32-row block of y for
+  // C y.  ||y||^2 is formed by every wave alike, so no reduction across waves
+  // is needed: each lane squares entries l and l + 64, then a sum over the
+  // wave by DPP moves and two lane-half swaps (every lane ends with the same
+  // bits).  The step's scale 1/||y_k|| uses the hardware reciprocal square
+  // root (the direction does not depend on the scale; v is normalised in fp64
+  // below).
+  auto norm2 = [&](int buf) {
+    const float y0 = sY[buf][l];
+    float q = y0 * y0;
+    if constexpr (D > 64) {
+      const float y1 = sY[buf][l + 64];
+      q = fmaf(y1, y1, q);
+    }
+    q += dpp_f32<0xB1>(q);   // quad_perm [1,0,3,2]
+    q += dpp_f32<0x4E>(q);   // quad_perm [2,3,0,1]
+    q += dpp_f32<0x141>(q);  // row_half_mirror
+    q += dpp_f32<0x140>(q);  // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+    q = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);  // rows 0+1, 2+3 of 16 lanes
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  };
+  int cur = 0, last = 0;
+  float nl = 1.0f;  // ||y_last||^2
+  for (int it = 0; it < iters; ++it) {
+    const float nrm2 = norm2(cur);
+    if (nrm2 == 0.0f) break;  // C v = 0: keep the previous direction
+    last = cur;
+    nl = nrm2;
+    const float inv = __builtin_amdgcn_rsqf(nrm2);
+    float wv = 0.0f;
+    if (gw) {
+      // y read two row blocks at a time (fewer registers: four workgroups per CU)
+      float part[NB];
+#pragma unroll
+      for (int b0 = 0; b0 < NB; b0 += 2) {
+        f32x4 yv[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) yv[j][g] = *(const f32x4*)&sY[cur][(b0 + j) * 32 + 8 * g + 4 * h];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          part[b0 + j] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part[b0 + j] = fmaf(cf[b0 + j][i], yv[j][i >> 2][i & 3], part[b0 + j]);
+        }
+      }
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) wv += part[bi];
+      wv = half_sum(wv) * inv;
+    }
+    const int nxt = cur ^ 1;
+    if (gw && h == 0) sY[nxt][w * 32 + ln] = wv;
+    __syncthreads();
+    cur = nxt;
+  }
+  {
+    const float nrm2 = norm2(cur);
+    if (nrm2 != 0.0f) {
+      last = cur;
+      nl = nrm2;
+    }
+  }
+  const double vinv = 1.0 / sqrt((double)nl);
+  if (tid < D) sV[tid] = (double)sY[last][tid] * vinv;
+  __syncthreads();
+}
+
 // ---- small nodes ------------------------------------------------------------
 // Nodes of at most kSmallRows rows (the deep levels: thousands of nodes, each a
 // chain of latencies) run with a lighter state so that four workgroups share
@@ -950,82 +1030,7 @@ __global__ __launch_bounds__(kNodeThreads) __attribute__((amdgpu_waves_per_eu(4,
       for (int i = 0; i < 16; ++i)
         cf[bi][i] = (float)((double)acc[bi][i] - sS[bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)] * sc);
   }
-  if (tid < D) sY[0][tid] = 1.0f / sqrtf((float)D);
-  __syncthreads();
-  // Every lane reads the rows 8g + 4h + 0..3 of each 32-row block of y for
-  // C y.  ||y||^2 is formed by every wave alike, so no reduction across waves
-  // is needed: each lane squares entries l and l + 64, then a sum over the
-  // wave by DPP moves and two lane-half swaps (every lane ends with the same
-  // bits).  The step's scale 1/||y_k|| uses the hardware reciprocal square
-  // root (the direction does not depend on the scale; v is normalised in fp64
-  // below).
-  auto read_y = [&](int buf, f32x4 (&yv)[NB][4]) {
-#pragma unroll
-    for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) yv[bi][g] = *(const f32x4*)&sY[buf][bi * 32 + 8 * g + 4 * h];
-  };
-  auto norm2 = [&](int buf) {
-    const float y0 = sY[buf][l];
-    float q = y0 * y0;
-    if constexpr (D > 64) {
-      const float y1 = sY[buf][l + 64];
-      q = fmaf(y1, y1, q);
-    }
-    q += dpp_f32<0xB1>(q);   // quad_perm [1,0,3,2]
-    q += dpp_f32<0x4E>(q);   // quad_perm [2,3,0,1]
-    q += dpp_f32<0x141>(q);  // row_half_mirror
-    q += dpp_f32<0x140>(q);  // row_mirror
-    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false, false);
-    q = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);  // rows 0+1, 2+3 of 16 lanes
-    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
-    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-  };
-  int cur = 0, last = 0;
-  float nl = 1.0f;  // ||y_last||^2
-  for (int it = 0; it < p.iters; ++it) {
-    const float nrm2 = norm2(cur);
-    if (nrm2 == 0.0f) break;  // C v = 0: keep the previous direction
-    last = cur;
-    nl = nrm2;
-    const float inv = __builtin_amdgcn_rsqf(nrm2);
-    float wv = 0.0f;
-    if (gw) {
-      // y read two row blocks at a time (fewer registers: four workgroups per CU)
-      float part[NB];
-#pragma unroll
-      for (int b0 = 0; b0 < NB; b0 += 2) {
-        f32x4 yv[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) yv[j][g] = *(const f32x4*)&sY[cur][(b0 + j) * 32 + 8 * g + 4 * h];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          part[b0 + j] = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) part[b0 + j] = fmaf(cf[b0 + j][i], yv[j][i >> 2][i & 3], part[b0 + j]);
-        }
-      }
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi) wv += part[bi];
-      wv = half_sum(wv) * inv;
-    }
-    const int nxt = cur ^ 1;
-    if (gw && h == 0) sY[nxt][w * 32 + ln] = wv;
-    __syncthreads();
-    cur = nxt;
-  }
-  {
-    const float nrm2 = norm2(cur);
-    if (nrm2 != 0.0f) {
-      last = cur;
-      nl = nrm2;
-    }
-  }
-  const double vinv = 1.0 / sqrt((double)nl);
-  if (tid < D) sV[tid] = (double)sY[last][tid] * vinv;
-  __syncthreads();
+  power_f32<D>(cf, sY, sV, p.iters);
   const double mv = wave_sum_f64(tid < D ? (sR[tid] + sS[tid] * inv_n) * sV[tid] : 0.0);
   if (l == 0 && w < 4) sMu[w] = mv;
   __syncthreads();
@@ -1134,9 +1139,10 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
 template <int D, bool BF16>
 __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) {
   constexpr int E = kPartE<D, BF16>;
-  __shared__ double sS[D], sR[D], sV[D], sRed[2][4];
+  __shared__ double sS[D], sR[D], sV[D];
   __shared__ double sX[kSymPart<D, BF16> ? 4 : 1][2][kSymPart<D, BF16> ? 1024 : 1];
-  __shared__ __attribute__((aligned(16))) double sY[2][D];
+  __shared__ __attribute__((aligned(16))) float sY[2][D];
+  __shared__ double sMu[4];
   const int bh = blockIdx.y, slot = blockIdx.x;
   const Node nd = pddp_node(slot, p.level, p.Nq, p.G);
   if (nd.c <= 1) return;
@@ -1187,7 +1193,22 @@ __global__ __launch_bounds__(kNodeThreads) void pddp_power_kernel(PddpParams p) 
         cacc[bi][i] = red[D + (size_t)(32 * bi + 8 * (i >> 2) + 4 * h + (i & 3)) * D + 32 * w + ln];
   }
   __syncthreads();
-  const double muv = centre_and_iterate<D, D / 32>(cacc, sS, BF16 ? sR : nullptr, sV, sY, sRed, nd.n, p.iters);
+  // centred in fp64, iterated in fp32 (C rounded to fp32, as in the small-node
+  // kernel): the steps' latency chain is half the fp64 one's
+  const double inv_n = 1.0 / (double)nd.n;
+  float cf[D / 32][16];
+  if (w < D / 32) {
+    const double sc = sS[w * 32 + ln] * inv_n;
+#pragma unroll
+    for (int bi = 0; bi < D / 32; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cf[bi][i] = (float)(cacc[bi][i] - sS[bi * 32 + 8 * (i >> 2) + 4 * h + (i & 3)] * sc);
+  }
+  power_f32<D>(cf, sY, sV, p.iters);
+  const double mv = wave_sum_f64(tid < D ? ((BF16 ? sR[tid] : 0.0) + sS[tid] * inv_n) * sV[tid] : 0.0);
+  if (l == 0 && w < 4) sMu[w] = mv;
+  __syncthreads();
+  const double muv = (sMu[0] + sMu[1]) + (sMu[2] + sMu[3]);
   double* out = p.vec + node * (D + 1);
   if (tid < D) out[tid] = sV[tid];
   if (tid == 0) out[D] = muv;
