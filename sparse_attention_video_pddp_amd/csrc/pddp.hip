@@ -20,7 +20,9 @@
 //      centring removes any shift; below the root the many-workgroup levels
 //      form the sums of left children only and take a right child's as its
 //      parent's minus its sibling's) and the fixed-step power iteration
-//      v <- C v / ||C v|| from v0 = 1/sqrt(d) in fp64 (a zero product keeps v);
+//      v <- C v / ||C v|| from v0 = 1/sqrt(d) (a zero product keeps v): in
+//      fp64 in pddp_node_kernel, in fp32 on C rounded to fp32 in
+//      pddp_power_kernel and pddp_small_kernel, v normalised in fp64;
 //   3. projections p_i = x_i . v - (r + S/n) . v in fp64, keyed by float(p_i);
 //   4. the floor(c/2)*G members of smallest key, equal keys lowest position
 //      first, go left, the rest right, both in their previous order (members
