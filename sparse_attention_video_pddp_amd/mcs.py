@@ -371,4 +371,9 @@ class ChunkedCausalStream:
             with torch.cuda.stream(ts):
                 k.copy_(K_chunk)
                 v.copy_(V_chunk)
+            if ts != cur:
+                # the caller may free the chunk's rows once this returns: keep the
+                # allocator from handing their memory out before ts has read them
+                K_chunk.record_stream(ts)
+                V_chunk.record_stream(ts)
         return self.layer.step(Q, self.K, self.V, is_anchor, stream=ts)
