@@ -45,9 +45,9 @@ struct Checked {
 
 // The automatic anchor mode takes the single pass for rows of visible keys up
 // to this length.  Measured on the frame-causal video (4680 queries, 12
-// heads, d = 128, group + anchor per chunk): 4680 visible keys 1.17 ms single
-// against 1.36 ms two-pass, 9360 keys 1.47 against 1.51, 14040 keys 1.76
-// against 1.68, 32760 keys 3.11 against 2.52; the single pass re-reads the
+// heads, d = 128, group + anchor per chunk): 4680 visible keys 0.81 ms single
+// against 0.99 ms two-pass, 9360 keys 1.08 against 1.12, 14040 keys 1.36
+// against 1.27, 32760 keys 2.65 against 1.99; the single pass re-reads the
 // visible K rows for every group, the two-pass path writes and re-reads the
 // mass matrix and launches twice.
 constexpr int kSinglePassAutoKv = 12288;
