@@ -104,6 +104,7 @@ def load_traffic(kernel: str, config: str):
 
 CLOCK_FILE = os.path.join(ROOT, "profiles", "clock.json")
 N_XCD = 8  # GRBM_GUI_ACTIVE is summed over the chip's XCDs
+N_CU = 256  # texture units (one address and one data unit per CU) summed by the _sum counters
 
 
 def load_clock(kernel: str, config: str):
@@ -274,6 +275,7 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
     for path, _ in runs:
         rows = sorted(csv.DictReader(open(path)), key=lambda r: (int(r["Dispatch_Id"]), r["Counter_Name"]))
         prev, last_id = "", None
+        per = {}  # this run's counters of each dispatch, for ratios between counters of one dispatch
         for r in rows:
             k = _short_kernel(r["Kernel_Name"])
             if r["Dispatch_Id"] != last_id:
@@ -282,6 +284,7 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
             d = vals.setdefault(label, {})
             v = float(r["Counter_Value"])
             d.setdefault(r["Counter_Name"], []).append(v)
+            per.setdefault((label, r["Dispatch_Id"]), {})[r["Counter_Name"]] = v
             dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
             if r["Counter_Name"] == "MfmaFlopsBF16":
                 d.setdefault("tflops", []).append(v / dt / 1e12 if dt > 0 else 0.0)
@@ -290,10 +293,19 @@ def summarize_pmc(out: str, runs, title: str, note: str) -> None:
                 d.setdefault("mcycles", []).append(v / 1e6)
                 d.setdefault("cyc_per_ns", []).append(v / (dt * 1e9) if dt > 0 else 0.0)
                 d.setdefault("dur_us", []).append(dt * 1e6)
+        for (label, _), c in per.items():
+            d, gui = vals[label], c.get("GRBM_GUI_ACTIVE", 0.0)
+            # busy cycles summed over the units of every CU, against the dispatch's cycles per XCD
+            for name, key in (("TA_TA_BUSY_sum", "ta_busy"), ("TD_TD_BUSY_sum", "td_busy")):
+                if name in c and gui > 0:
+                    d.setdefault(key, []).append(100.0 * c[name] / N_CU / (gui / N_XCD))
+            if "SQ_WAIT_ANY" in c and c.get("SQ_WAVE_CYCLES", 0.0) > 0:
+                d.setdefault("wave_wait", []).append(100.0 * c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"])
     cols = [("MfmaUtil", "MFMA busy %", 1), ("tflops", "MFMA TFLOP/s", 1), ("LdsUtil", "LDS busy %", 1),
             ("LdsBankConflict", "bank-conflict cycles per LDS cycle", 3), ("VALUBusy", "VALU busy %", 1),
             ("dur_us", "duration (us)", 1), ("mcycles", "GRBM_GUI_ACTIVE (M cycles)", 2),
-            ("cyc_per_ns", "GRBM_GUI_ACTIVE per ns", 3)]
+            ("cyc_per_ns", "GRBM_GUI_ACTIVE per ns", 3), ("wave_wait", "waves waiting %", 1),
+            ("ta_busy", "texture address busy %", 1), ("td_busy", "texture data busy %", 1)]
     cols = [c for c in cols if any(c[0] in d for d in vals.values())]  # only counters of these runs
     config = os.environ.get("MCS_BENCH_CONFIG", "bidir5")
     clock = {}
